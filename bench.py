@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the NA3D forward kernel on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+
+A step is one na3d_fwd call over one batch of the synthetic workload (all
+inputs resident in HBM before timing starts).  The headline workload is the
+VAE-decoder tile (B=1, T=16, H=64, W=96, NH=8, HD=64, window 3x7x7).  Prints
+ONE JSON line with TFLOP/s (algorithmic FLOPs = 4*B*NH*T*H*W*KT*KH*KW*HD), the
+roofline of the kernel (HBM-bound at this arithmetic intensity: compulsory
+bytes = q, k, v read once + out written once) and the CPU oracle's throughput
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+HEADLINE = "decoder_tile"
+METRIC = "NA3D fwd TFLOP/s and % bf16 MFMA peak on 1 MI355X, (3,7,7)/(11,11,11)"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--all", action="store_true",
+                    help="one JSON line per workload (development use)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip the sampled parity check before timing")
+    return ap.parse_args()
+
+
+def time_kernel(fn, steps, warmup):
+    """Warm up, then time `steps` back-to-back launches.  Returns
+    (wall ms per step, kernel ms per launch from HIP events on the launch
+    stream)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return wall_ms, e0.elapsed_time(e1) / steps
+
+
+def sampled_check(q, k, v, window, out, seed, npts=400):
+    """Parity gate before timing (validate, then time): oracle vs GPU on
+    sampled outputs."""
+    import oracle
+    import torch
+
+    shape = tuple(q.shape)
+    rng = np.random.default_rng(seed)
+    pts = np.stack([rng.integers(0, s, npts) for s in shape[:5]], axis=1)
+    idx = tuple(torch.as_tensor(pts[:, i], device=q.device) for i in range(5))
+
+    def gather_window_inputs():
+        return q.cpu(), k.cpu(), v.cpu()
+
+    qc, kc, vc = gather_window_inputs()
+    ref = oracle.fwd_points(qc, kc, vc, window, pts)
+    got = out[idx].double().cpu().numpy()
+    diff = got - ref
+    rel = float(np.linalg.norm(diff) / np.linalg.norm(ref))
+    return rel, float(np.abs(diff).max()), (qc, kc, vc)
+
+
+def cpu_baseline(host_inputs, window, seed, target_s):
+    """Time the oracle (as it stands) on a bounded random sample of the
+    workload's queries; returns TFLOP/s, threads and a description."""
+    import oracle
+
+    qc, kc, vc = host_inputs
+    shape = tuple(qc.shape)
+    KT, KH, KW = window
+    HD = shape[5]
+    per_query = 4 * KT * KH * KW * HD
+    rng = np.random.default_rng(seed + 17)
+    threads = oracle.max_threads(0)
+
+    def run(n):
+        pts = np.stack([rng.integers(0, s, n) for s in shape[:5]], axis=1)
+        t0 = time.perf_counter()
+        oracle.fwd_points(qc, kc, vc, window, pts)
+        return time.perf_counter() - t0
+
+    pilot_n = 2000
+    dt = run(pilot_n)
+    n = int(min(max(pilot_n * target_s / max(dt, 1e-6), pilot_n), 50_000_000))
+    dt = run(n)
+    total_q = int(np.prod(shape[:5]))
+    return {
+        "value": n * per_query / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d random query-heads of %d (%.2f%%), %.1f s of oracle time, "
+                  "double precision, OpenMP" % (n, total_q, 100.0 * n / total_q, dt),
+    }
+
+
+def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0):
+    import torch
+
+    import neighborhood_attention_amd as na
+    from na3d_inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(w.shape, w.seed, "cuda", w.k_outlier_frac, w.k_outlier_scale)
+    out = torch.empty_like(q)
+    fn = lambda: na.fwd(q, k, v, w.window, out=out)
+    fn()
+    torch.cuda.synchronize()
+    rel = mab = None
+    host = None
+    if check or cpu:
+        rel, mab, host = sampled_check(q, k, v, w.window, out, w.seed)
+        if rel > 1e-2 or mab > 5e-2:
+            raise SystemExit("parity gate failed on %s: rel_l2=%.3e max_abs=%.3e"
+                             % (name, rel, mab))
+    wall_ms, kern_ms = time_kernel(fn, steps, warmup)
+    tflops = w.flops / (wall_ms * 1e-3) / 1e12
+    kern_s = kern_ms * 1e-3
+    ai = w.flops / w.bytes
+    bound = "mfma" if ai > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
+    if bound == "hbm":
+        achieved, peak, unit = w.bytes / kern_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = w.flops / kern_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    plan = na.plan(w.shape, w.window)
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": name,
+            "shape_BTHWNH_HD": list(w.shape),
+            "window": list(w.window),
+            "seed": w.seed,
+            "tile": [plan["tile_t"], plan["tile_h"], plan["tile_w"]],
+            "workgroups": plan["workgroups"],
+        },
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 5),
+        "effective_GBps": round(w.bytes / (wall_ms * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": bound,
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+        },
+        "kernel_us": round(kern_ms * 1e3, 2),
+        "parity_sampled": {"rel_l2": rel, "max_abs": mab},
+    }
+    if cpu and host is not None:
+        rec["cpu_baseline"] = cpu_baseline(host, w.window, w.seed, cpu_s)
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        return 1
+    if args.all:
+        from na3d_inputs import WORKLOADS
+        for name in WORKLOADS:
+            rec = bench_workload(name, args.steps, args.warmup, check=not args.no_check,
+                                 cpu=False)
+            print(json.dumps(rec), flush=True)
+        return 0
+    rec = bench_workload(args.workload, args.steps, args.warmup, check=not args.no_check,
+                         cpu=not args.no_cpu_baseline, cpu_s=args.cpu_seconds)
+    if args.workload == HEADLINE:
+        # the metric also names the 11x11x11 window: report it beside the headline
+        lw = bench_workload("large_window", args.steps, args.warmup, check=False, cpu=False)
+        rec["large_window_11x11x11"] = {
+            "value": lw["value"], "unit": "TFLOP/s", "mfma_peak_frac": lw["mfma_peak_frac"],
+            "ms_per_step": lw["ms_per_step"], "roofline": lw["roofline"]}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

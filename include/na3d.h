@@ -1,0 +1,99 @@
+/*
+ * na3d.h -- C ABI of the MI355X (gfx950) library for the forward pass of
+ * 3-D neighborhood attention (NA3D).
+ *
+ * Operation (ROCm/aiter PR "Add 3D neighborhood flash attention (na3d_flash)",
+ * Motivation and Technical Details):
+ *   For every batch b, head n and query token (t,h,w) of a T x H x W grid,
+ *     out[b,t,h,w,n,:] = sum_j softmax_j( q[b,t,h,w,n,:] . k[b,j,n,:] ) v[b,j,n,:]
+ *   where j runs over the KT x KH x KW box of key tokens starting, per axis, at
+ *     start(i, K, L) = clamp(i - K/2, 0, L - K)          (integer K/2)
+ *   i.e. the box is centred on the query and shifted inward at a border so it
+ *   always holds exactly KT*KH*KW keys.  Q is expected to be pre-multiplied
+ *   by head_dim^-0.5 by the caller; the library applies no further scale.
+ *   Scores, softmax and the weighted sum are accumulated in fp32; the softmax
+ *   weights are rounded to bf16 before the weighted sum (flash-attention style);
+ *   the output is rounded to bf16 (round to nearest even).
+ *
+ * Layout: q, k, v and out are contiguous bf16 tensors of shape
+ *   (B, T, H, W, NH, HD), HD fastest (the public launcher's layout on the
+ *   same page).  Element (b,t,h,w,n,d) is at
+ *   ((((b*T + t)*H + h)*W + w)*NH + n)*HD + d.
+ *
+ * Ownership: every pointer is a DEVICE pointer owned by the caller.  The
+ *   library allocates nothing, frees nothing and keeps no pointer after a
+ *   call returns.  out must not overlap q, k or v; q, k and v may alias each
+ *   other (they are only read).
+ *
+ * Asynchrony: na3d_fwd enqueues its kernel on `stream` (a hipStream_t; NULL
+ *   means the default stream) and returns without synchronising.  A fault
+ *   during execution is reported by the caller's next synchronising call.
+ *
+ * Errors: every function returns 0 on success or a negative NA3D_ERR_* code.
+ *   All argument checks run before any device call, so a rejected call has
+ *   no effect on the device.  Nothing is printed and no exception crosses
+ *   the ABI.
+ */
+#ifndef NA3D_H_
+#define NA3D_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NA3D_OK 0
+#define NA3D_ERR_NULL (-1)     /* a tensor pointer is NULL */
+#define NA3D_ERR_SHAPE (-2)    /* a dimension is < 1, or the tensor is too large */
+#define NA3D_ERR_WINDOW (-3)   /* a window extent is < 1 or exceeds its grid axis */
+#define NA3D_ERR_HEAD_DIM (-4) /* HD is not one of 16, 32, 64, 128, 256 */
+#define NA3D_ERR_ALIGN (-5)    /* a pointer is not 16-byte aligned */
+#define NA3D_ERR_OVERLAP (-6)  /* out overlaps q, k or v */
+#define NA3D_ERR_DEVICE (-7)   /* the current HIP device is not gfx950 */
+#define NA3D_ERR_LAUNCH (-8)   /* the kernel launch was rejected by HIP */
+
+/*
+ * Forward pass of 3-D neighborhood attention.
+ *   q, k, v : device pointers, bf16, (B,T,H,W,NH,HD) contiguous, 16-B aligned
+ *   out     : device pointer, bf16, same shape; fully overwritten
+ *   B,T,H,W : batch and grid extents (>= 1)
+ *   NH, HD  : heads and head dimension (HD in {16,32,64,128,256})
+ *   KT,KH,KW: window extents, 1 <= K <= the matching grid extent (even
+ *             extents are accepted and follow the same start formula)
+ *   stream  : hipStream_t to enqueue on, or NULL for the default stream
+ * Returns NA3D_OK or a negative NA3D_ERR_* code.
+ */
+int na3d_fwd(const void* q, const void* k, const void* v, void* out, int B,
+             int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
+             void* stream);
+
+/*
+ * The argument checks of na3d_fwd alone, without touching any device
+ * (NULL pointers, dimensions, window extents, head dimension, alignment,
+ * overlap).  Returns NA3D_OK or the code na3d_fwd would return.
+ */
+int na3d_check_args(const void* q, const void* k, const void* v,
+                    const void* out, int B, int T, int H, int W, int NH,
+                    int HD, int KT, int KH, int KW);
+
+/* Static, NUL-terminated description of a status code. */
+const char* na3d_status_string(int status);
+
+/*
+ * Launch plan na3d_fwd would use for these sizes, without touching a device:
+ * plan[0] = kernel family id, plan[1] = tile extent along T, plan[2] = tile
+ * extent along H, plan[3] = tile extent along W, plan[4] = workgroups,
+ * plan[5] = threads per workgroup, plan[6] = dynamic LDS bytes, plan[7] = K/V
+ * planes staged per workgroup.  `plan` must hold 8 ints.  Returns NA3D_OK or
+ * an NA3D_ERR_* code for invalid sizes.
+ */
+int na3d_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH,
+              int KW, int* plan);
+
+/* Library ABI version (incremented on incompatible changes). */
+int na3d_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NA3D_H_ */

@@ -1,0 +1,138 @@
+"""Python binding of the MI355X NA3D forward library (``libna3d.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/na3d.h``.  torch supplies
+device memory and the current stream.  There is no CPU or eager fallback:
+if the library is missing or the device is not gfx950, calls raise.
+
+    out = neighborhood_attention_amd.fwd(q, k, v, kernel_size=(3, 7, 7))
+
+mirrors ``na3d_flash_attn(q, k, v, kernel_size)`` of the ROCm/aiter PR
+"Add 3D neighborhood flash attention (na3d_flash)" (Technical Details):
+(B, T, H, W, NH, HD) bf16 tensors, Q pre-scaled by head_dim**-0.5.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libna3d.so")
+
+NA3D_OK = 0
+NA3D_ERR_NULL = -1
+NA3D_ERR_SHAPE = -2
+NA3D_ERR_WINDOW = -3
+NA3D_ERR_HEAD_DIM = -4
+NA3D_ERR_ALIGN = -5
+NA3D_ERR_OVERLAP = -6
+NA3D_ERR_DEVICE = -7
+NA3D_ERR_LAUNCH = -8
+
+EXPORTS = ("na3d_fwd", "na3d_check_args", "na3d_status_string", "na3d_plan",
+           "na3d_abi_version")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class NA3DError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+def load(path: str = LIB_PATH):
+    """Load (building first if absent) and type the C ABI."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            from . import _build
+            _build.build()
+        lib = ctypes.CDLL(path)
+        i32, p = ctypes.c_int, ctypes.c_void_p
+        lib.na3d_fwd.argtypes = [p, p, p, p] + [i32] * 9 + [p]
+        lib.na3d_fwd.restype = i32
+        lib.na3d_check_args.argtypes = [p, p, p, p] + [i32] * 9
+        lib.na3d_check_args.restype = i32
+        lib.na3d_status_string.argtypes = [i32]
+        lib.na3d_status_string.restype = ctypes.c_char_p
+        lib.na3d_plan.argtypes = [i32] * 9 + [ctypes.POINTER(i32)]
+        lib.na3d_plan.restype = i32
+        lib.na3d_abi_version.argtypes = []
+        lib.na3d_abi_version.restype = i32
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load().na3d_status_string(int(status)).decode()
+
+
+def check_args(q_ptr, k_ptr, v_ptr, out_ptr, shape, kernel_size) -> int:
+    """Host-only argument check on raw addresses (no device access)."""
+    B, T, H, W, NH, HD = (int(x) for x in shape)
+    KT, KH, KW = (int(x) for x in kernel_size)
+    return load().na3d_check_args(q_ptr, k_ptr, v_ptr, out_ptr, B, T, H, W, NH, HD,
+                                  KT, KH, KW)
+
+
+def plan(shape, kernel_size) -> dict:
+    B, T, H, W, NH, HD = (int(x) for x in shape)
+    KT, KH, KW = (int(x) for x in kernel_size)
+    buf = (ctypes.c_int * 8)()
+    rc = load().na3d_plan(B, T, H, W, NH, HD, KT, KH, KW, buf)
+    if rc != NA3D_OK:
+        raise NA3DError(rc, "na3d_plan")
+    keys = ("family", "tile_t", "tile_h", "tile_w", "workgroups", "threads",
+            "lds_bytes", "planes")
+    return dict(zip(keys, list(buf)))
+
+
+def fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, shape, kernel_size,
+            stream: int = 0) -> None:
+    """Call na3d_fwd on raw device addresses; raises NA3DError on failure."""
+    B, T, H, W, NH, HD = (int(x) for x in shape)
+    KT, KH, KW = (int(x) for x in kernel_size)
+    rc = load().na3d_fwd(q_ptr, k_ptr, v_ptr, out_ptr, B, T, H, W, NH, HD, KT, KH, KW,
+                         stream)
+    if rc != NA3D_OK:
+        raise NA3DError(rc, "na3d_fwd")
+
+
+def fwd(q, k, v, kernel_size, out=None):
+    """3-D neighborhood attention forward on (B,T,H,W,NH,HD) bf16 CUDA tensors.
+
+    Returns ``out`` (allocated with ``torch.empty_like(q)`` when not given).
+    The kernel is enqueued on torch's current stream.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if t.dtype != torch.bfloat16:
+            raise TypeError("%s must be bfloat16, got %s" % (name, t.dtype))
+        if t.device.type != "cuda":
+            raise ValueError("%s must be a GPU tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if q.dim() != 6:
+        raise ValueError("expected (B,T,H,W,NH,HD) tensors, got %d dims" % q.dim())
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v shapes differ: %s %s %s" % (q.shape, k.shape, v.shape))
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v are on different devices")
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), q.shape,
+                kernel_size, stream)
+    return out
