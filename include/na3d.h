@@ -50,6 +50,7 @@ extern "C" {
 #define NA3D_ERR_OVERLAP (-6)  /* out overlaps q, k or v */
 #define NA3D_ERR_DEVICE (-7)   /* the current HIP device is not gfx950 */
 #define NA3D_ERR_LAUNCH (-8)   /* the kernel launch was rejected by HIP */
+#define NA3D_ERR_CONFIG (-9)   /* an explicit launch configuration cannot run the sizes */
 
 /*
  * Forward pass of 3-D neighborhood attention.
@@ -80,7 +81,8 @@ const char* na3d_status_string(int status);
 
 /*
  * Launch plan na3d_fwd would use for these sizes, without touching a device:
- * plan[0] = kernel family id, plan[1] = tile extent along T, plan[2] = tile
+ * plan[0] = kernel family id (1 general, 2 rolling), plan[1] = query planes
+ * per workgroup, plan[2] = tile
  * extent along H, plan[3] = tile extent along W, plan[4] = workgroups,
  * plan[5] = threads per workgroup, plan[6] = dynamic LDS bytes, plan[7] = K/V
  * planes staged per workgroup.  `plan` must hold 8 ints.  Returns NA3D_OK or
@@ -88,6 +90,32 @@ const char* na3d_status_string(int status);
  */
 int na3d_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH,
               int KW, int* plan);
+
+/*
+ * na3d_fwd with an explicit launch configuration, for tuning sweeps and for
+ * testing each kernel instantiation on its own.
+ *   family : 0 = automatic (exactly na3d_fwd), 1 = general family (one query
+ *            plane per workgroup, no limit on window size), 2 = rolling
+ *            family (a run of query planes per workgroup)
+ *   variant: rolling instantiation, 0 .. na3d_num_variants()-1 (ignored
+ *            otherwise); each is compiled for one head dimension
+ *   tile_t : query planes per rolling workgroup, 0 = automatic
+ * Same pointer/layout/ownership/stream contract as na3d_fwd.  Returns
+ * NA3D_ERR_CONFIG when the configuration cannot run these sizes (wrong head
+ * dimension for the variant, window union or halo beyond its static limits,
+ * or more concurrently active query planes than its slots).
+ */
+int na3d_fwd_config(const void* q, const void* k, const void* v, void* out,
+                    int B, int T, int H, int W, int NH, int HD, int KT, int KH,
+                    int KW, int family, int variant, int tile_t, void* stream);
+
+/* na3d_plan for an explicit configuration (see na3d_fwd_config). */
+int na3d_plan_config(int B, int T, int H, int W, int NH, int HD, int KT,
+                     int KH, int KW, int family, int variant, int tile_t,
+                     int* plan);
+
+/* Number of rolling-family instantiations compiled into the library. */
+int na3d_num_variants(void);
 
 /* Library ABI version (incremented on incompatible changes). */
 int na3d_abi_version(void);

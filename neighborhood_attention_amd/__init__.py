@@ -29,9 +29,12 @@ NA3D_ERR_ALIGN = -5
 NA3D_ERR_OVERLAP = -6
 NA3D_ERR_DEVICE = -7
 NA3D_ERR_LAUNCH = -8
+NA3D_ERR_CONFIG = -9
 
 EXPORTS = ("na3d_fwd", "na3d_check_args", "na3d_status_string", "na3d_plan",
-           "na3d_abi_version")
+           "na3d_fwd_config", "na3d_plan_config", "na3d_num_variants", "na3d_abi_version")
+PLAN_KEYS = ("family", "tile_t", "tile_h", "tile_w", "workgroups", "threads", "lds_bytes",
+             "planes")
 
 _lock = threading.Lock()
 _lib = None
@@ -62,6 +65,12 @@ def load(path: str = LIB_PATH):
         lib.na3d_status_string.restype = ctypes.c_char_p
         lib.na3d_plan.argtypes = [i32] * 9 + [ctypes.POINTER(i32)]
         lib.na3d_plan.restype = i32
+        lib.na3d_fwd_config.argtypes = [p, p, p, p] + [i32] * 12 + [p]
+        lib.na3d_fwd_config.restype = i32
+        lib.na3d_plan_config.argtypes = [i32] * 12 + [ctypes.POINTER(i32)]
+        lib.na3d_plan_config.restype = i32
+        lib.na3d_num_variants.argtypes = []
+        lib.na3d_num_variants.restype = i32
         lib.na3d_abi_version.argtypes = []
         lib.na3d_abi_version.restype = i32
         _lib = lib
@@ -80,34 +89,45 @@ def check_args(q_ptr, k_ptr, v_ptr, out_ptr, shape, kernel_size) -> int:
                                   KT, KH, KW)
 
 
-def plan(shape, kernel_size) -> dict:
+def plan(shape, kernel_size, family: int = 0, variant: int = 0, tile_t: int = 0) -> dict:
+    """Launch plan for these sizes (automatic, or an explicit configuration)."""
     B, T, H, W, NH, HD = (int(x) for x in shape)
     KT, KH, KW = (int(x) for x in kernel_size)
     buf = (ctypes.c_int * 8)()
-    rc = load().na3d_plan(B, T, H, W, NH, HD, KT, KH, KW, buf)
+    rc = load().na3d_plan_config(B, T, H, W, NH, HD, KT, KH, KW, int(family), int(variant),
+                                 int(tile_t), buf)
     if rc != NA3D_OK:
         raise NA3DError(rc, "na3d_plan")
-    keys = ("family", "tile_t", "tile_h", "tile_w", "workgroups", "threads",
-            "lds_bytes", "planes")
-    return dict(zip(keys, list(buf)))
+    return dict(zip(PLAN_KEYS, list(buf)))
+
+
+def num_variants() -> int:
+    return int(load().na3d_num_variants())
 
 
 def fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, shape, kernel_size,
-            stream: int = 0) -> None:
-    """Call na3d_fwd on raw device addresses; raises NA3DError on failure."""
+            stream: int = 0, config=None) -> None:
+    """Call na3d_fwd (or na3d_fwd_config when ``config`` = (family, variant,
+    tile_t) is given) on raw device addresses; raises NA3DError on failure."""
     B, T, H, W, NH, HD = (int(x) for x in shape)
     KT, KH, KW = (int(x) for x in kernel_size)
-    rc = load().na3d_fwd(q_ptr, k_ptr, v_ptr, out_ptr, B, T, H, W, NH, HD, KT, KH, KW,
-                         stream)
+    if config is None:
+        rc = load().na3d_fwd(q_ptr, k_ptr, v_ptr, out_ptr, B, T, H, W, NH, HD, KT, KH, KW,
+                             stream)
+    else:
+        fam, var, tt = (int(x) for x in config)
+        rc = load().na3d_fwd_config(q_ptr, k_ptr, v_ptr, out_ptr, B, T, H, W, NH, HD, KT,
+                                    KH, KW, fam, var, tt, stream)
     if rc != NA3D_OK:
         raise NA3DError(rc, "na3d_fwd")
 
 
-def fwd(q, k, v, kernel_size, out=None):
+def fwd(q, k, v, kernel_size, out=None, config=None):
     """3-D neighborhood attention forward on (B,T,H,W,NH,HD) bf16 CUDA tensors.
 
     Returns ``out`` (allocated with ``torch.empty_like(q)`` when not given).
-    The kernel is enqueued on torch's current stream.
+    The kernel is enqueued on torch's current stream.  ``config`` =
+    (family, variant, tile_t) forces a launch configuration (tuning/testing).
     """
     import torch
 
@@ -134,5 +154,5 @@ def fwd(q, k, v, kernel_size, out=None):
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), q.shape,
-                kernel_size, stream)
+                kernel_size, stream, config)
     return out

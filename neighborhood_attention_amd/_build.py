@@ -6,7 +6,8 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "na3d.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f)
+           for f in ("na3d.cpp", "kernel_general.hip", "kernel_roll.hip")]
 LIB = os.path.join(HERE, "libna3d.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -14,13 +15,21 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no NaN inputs are in contract: max needs no NaN-quieting; infinities
+    # (the -inf window masks) are still honoured
+    "-fno-honor-nans",
+    # MFMA accumulators in VGPRs: the rare rescale path multiplies them with
+    # VALU ops, which cannot read AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
+# .cpp sources go through the HIP compiler as well
+LANG = ["-x", "hip"]
 
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
+    cmd = [HIPCC] + FLAGS + LANG + SOURCES + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)

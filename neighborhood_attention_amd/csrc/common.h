@@ -1,0 +1,110 @@
+// common.h -- types and helpers shared by the NA3D kernel families and the
+// host-side planner (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace na3d {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Swizzled, unpadded staging layout (rolling family).  A staged row is HD*2
+// bytes = HD/8 chunks of 16 bytes; logical chunk c of row r is stored at
+// physical chunk c ^ swz(r).  swz depends only on r mod 16, and the operand
+// reads of a 32-key block start at multiples of 16 rows, so the XOR term is a
+// per-lane constant.  The function is chosen so that both operand reads are
+// free of LDS bank conflicts (64 banks of 4 bytes):
+//   K read  -- 16 lanes take the same logical chunk of 16 consecutive rows;
+//   V read  -- the transpose read takes 8 bytes from each of 4 consecutive
+//              rows per 4 lanes, i.e. one 32-byte chunk pair per row.
+__host__ __device__ constexpr int swz(int hd, int r) {
+  return hd == 16   ? (r >> 3) & 1
+         : hd == 32 ? (r >> 2) & 3
+         : hd == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))
+                    : ((r & 7) << 1) | ((r >> 3) & 1);
+}
+
+// Inward-shifted window start on one axis: clamp(i - K/2, 0, L - K).
+__host__ __device__ __forceinline__ int win_start(int i, int K, int L) {
+  int s = i - (K >> 1);
+  s = s < 0 ? 0 : s;
+  return s > L - K ? L - K : s;
+}
+
+// Spread consecutive logical tiles over one XCD: the dispatcher hands
+// workgroup i to XCD i % 8, so XCD x receives logical tiles [x*n/8, (x+1)*n/8)
+// in order and neighbouring tiles (which share K/V halo rows) meet in one L2.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  const int per = n >> 3;
+  const int rem = n & 7;
+  if (i >= n - rem) return i;  // the ragged tail keeps its position
+  return (i & 7) * per + (i >> 3);
+}
+
+struct Problem {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int B, T, H, W, NH;
+  int KT, KH, KW;
+};
+
+// Launch description chosen by the host planner.
+struct Launch {
+  int family;      // 1 = general (one query plane per workgroup), 2 = rolling
+  int variant;     // index into the family's instantiation table
+  int tile_t, tile_h, tile_w;
+  int tiles_t, tiles_h, tiles_w;
+  int64_t wgs;
+  int threads;
+  int lds_rows;    // rows of each K and V staging buffer
+  int lds_bytes;
+  int planes;      // K/V planes staged per workgroup (maximum)
+};
+
+// Instantiations of the rolling family: index, head dim, query block
+// (QH x QW = 16), wave grid (WH block rows x WT query-plane phases), query-plane
+// slots per wave, the most full 32-key blocks a wave's window union may hold,
+// and the number of staged plane buffers.
+#define NA3D_ROLL_VARIANTS(X)          \
+  X(0, 16, 2, 8, 2, 2, 2, 4, 2)        \
+  X(1, 32, 2, 8, 2, 2, 2, 4, 2)        \
+  X(2, 64, 2, 8, 2, 2, 2, 4, 2)        \
+  X(3, 64, 2, 8, 2, 2, 2, 4, 1)        \
+  X(4, 64, 2, 8, 4, 1, 4, 4, 2)        \
+  X(5, 64, 2, 8, 1, 4, 2, 4, 2)        \
+  X(6, 64, 4, 4, 1, 4, 4, 7, 1)        \
+  X(7, 64, 4, 4, 2, 2, 4, 7, 1)        \
+  X(8, 64, 4, 4, 1, 8, 2, 7, 1)        \
+  X(9, 128, 2, 8, 2, 2, 2, 4, 1)       \
+  X(10, 128, 2, 8, 2, 2, 2, 4, 2)      \
+  X(11, 128, 2, 8, 1, 4, 2, 4, 1)      \
+  X(12, 256, 2, 8, 1, 2, 2, 4, 1)
+
+struct RollVariant {
+  int hd, qh, qw, wh, wt, ns, maxb, nbuf;
+};
+
+constexpr RollVariant kRollVariants[] = {
+#define NA3D_ROLL_ENTRY(i, HD, QH, QW, WH, WT, NS, MAXB, NBUF) \
+  {HD, QH, QW, WH, WT, NS, MAXB, NBUF},
+    NA3D_ROLL_VARIANTS(NA3D_ROLL_ENTRY)
+#undef NA3D_ROLL_ENTRY
+};
+constexpr int kNumRollVariants = sizeof(kRollVariants) / sizeof(kRollVariants[0]);
+
+int launch_general(const Problem& p, const Launch& l, int hd, hipStream_t s);
+int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s);
+
+}  // namespace na3d

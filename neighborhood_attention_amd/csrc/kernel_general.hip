@@ -1,46 +1,37 @@
-// na3d.hip -- MI355X (gfx950) forward pass of 3-D neighborhood attention.
+// kernel_general.hip -- the general NA3D forward family (gfx950).
 //
 // Operation: ROCm/aiter PR "Add 3D neighborhood flash attention (na3d_flash)",
 // Motivation (each query token attends to a KT x KH x KW box of keys) and
 // Technical Details (windows shifted inward at borders so each holds exactly
 // KT*KH*KW keys; Q pre-scaled by head_dim^-0.5; online softmax in log2 space).
 //
-// Structure of one workgroup (WG): batch b, head n, query plane t and a
-// BH x BW spatial tile of queries.  The WG walks the KT key planes of its
-// window; for each it stages the tile's K/V halo (the union of its queries'
-// windows) in LDS with 16-byte loads, then every wave processes its own
-// 16-query block (QH x QW queries) against the union of that block's windows,
-// flattened and cut into 32-key blocks:
+// One workgroup (WG) = batch b, head n, one query plane t and an 8 x 8
+// spatial tile of queries.  The WG walks the KT key planes of its window; for
+// each it stages the tile's K/V halo (the union of its queries' windows) in
+// LDS, in chunks when the halo exceeds the LDS budget, and every wave handles
+// its 4 x 4 query block against the union of that block's windows, flattened
+// and cut into 32-key blocks:
 //   S^T (16 keys x 16 queries) = K . Q^T          bf16 MFMA 16x16x32
 //   window mask from the per-query clamped starts  (out-of-window -> -inf)
 //   online softmax per query, fp32, exp2
 //   O^T (16 hd x 16 queries) += V^T . P^T          bf16 MFMA 16x16x32
 // The transposed orientation keeps one query per lane, so the running max
 // and sum of a query live in the 4 lanes that share it, and the score
-// accumulator of S^T is already the B operand of the P.V product (no shuffle).
-// V^T operands come straight from row-major LDS through the gfx950 transpose
-// read (ds_read_b64_tr_b16), which also gathers arbitrary key rows.
-#include <hip/hip_runtime.h>
+// accumulator of S^T is already the B operand of the P.V product.  V^T
+// operands come straight from row-major LDS through the gfx950 transpose read
+// (ds_read_b64_tr_b16), which also gathers arbitrary key rows.
+//
+// This family has no static limit on window size or union shape (key
+// coordinates are decoded per block); the rolling family is used wherever its
+// register-resident tables fit.
+#include "common.h"
 
-#include <atomic>
-#include <cstdint>
-#include <cstring>
-
-#include "../../include/na3d.h"
-
+namespace na3d {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-constexpr int kWave = 64;
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kLdsPad = 16;  // bytes of padding per staged K/V row
 
-struct Args {
+struct GeneralArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
@@ -50,13 +41,6 @@ struct Args {
   int tiles_h, tiles_w;
   int lds_rows;  // capacity of each of the K and V staging buffers, in rows
 };
-
-// clamp(i - K/2, 0, L - K)
-__device__ __forceinline__ int win_start(int i, int K, int L) {
-  int s = i - (K >> 1);
-  s = s < 0 ? 0 : s;
-  return s > L - K ? L - K : s;
-}
 
 __device__ __forceinline__ void divmod(int u, int d, int& qo, int& ro) {
   qo = u / d;
@@ -74,23 +58,13 @@ __device__ __forceinline__ int union_keys_before(int r, int oh, int ow, int uhn,
   return hr * uw + wr;
 }
 
-// Spread consecutive logical tiles over one XCD: hardware hands workgroup i
-// to XCD i % 8, so XCD x receives logical tiles [x*n/8, (x+1)*n/8) in order
-// and neighbouring tiles (which share K/V halo rows) meet in the same L2.
-__device__ __forceinline__ int xcd_remap(int i, int n) {
-  const int per = n >> 3;
-  const int rem = n & 7;
-  if (i >= n - rem) return i;  // the ragged tail keeps its position
-  return (i & 7) * per + (i >> 3);
-}
-
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 template <int HD, int QH, int QW, int WH, int WW>
 __global__ void __launch_bounds__(kWave * WH * WW)
-na3d_fwd_plane_kernel(const Args a) {
+na3d_fwd_general_kernel(const GeneralArgs a) {
   static_assert(QH * QW == 16, "a wave owns 16 queries");
   constexpr int BH = WH * QH;
   constexpr int BW = WW * QW;
@@ -307,169 +281,43 @@ na3d_fwd_plane_kernel(const Args a) {
   }
 }
 
-// ------------------------------------------------------------------ host side
+
 constexpr int kQH = 4, kQW = 4, kWH = 2, kWW = 2;  // 8 x 8 query tile, 4 waves
-constexpr int kMaxLdsBytes = 80 * 1024;            // two workgroups per CU
-
-int head_dim_ok(int hd) { return hd == 16 || hd == 32 || hd == 64 || hd == 128 || hd == 256; }
-
-bool overlaps(const void* a, const void* b, size_t bytes) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + bytes && y < x + bytes;
-}
-
-struct Plan {
-  int family, bt, bh, bw;
-  int64_t wgs;
-  int threads, lds_bytes, planes;
-  int tiles_h, tiles_w, lds_rows;
-};
-
-int ceil_div(int a, int b) { return (a + b - 1) / b; }
-
-int make_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, Plan* p) {
-  const int BH = kWH * kQH, BW = kWW * kQW;
-  p->family = 1;
-  p->bt = 1;
-  p->bh = BH;
-  p->bw = BW;
-  p->tiles_h = ceil_div(H, BH);
-  p->tiles_w = ceil_div(W, BW);
-  p->wgs = (int64_t)B * NH * T * p->tiles_h * p->tiles_w;
-  p->threads = kWave * kWH * kWW;
-  const int row = HD * 2 + kLdsPad;
-  const int max_halo = (std::min(BH + KH - 1, H)) * (std::min(BW + KW - 1, W));
-  const int cap = kMaxLdsBytes / (2 * row);
-  p->lds_rows = std::min(max_halo, cap);
-  p->lds_bytes = 2 * p->lds_rows * row;
-  p->planes = KT;
-  if (p->wgs > 0x7fffffff) return NA3D_ERR_SHAPE;
-  return NA3D_OK;
-}
-
-int check_sizes(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW) {
-  if (B < 1 || T < 1 || H < 1 || W < 1 || NH < 1 || HD < 1) return NA3D_ERR_SHAPE;
-  if (!head_dim_ok(HD)) return NA3D_ERR_HEAD_DIM;
-  // element offsets of one batch entry are formed in 64-bit; grid extents
-  // themselves must keep per-axis products in 32-bit range
-  if ((int64_t)T * H * W > (int64_t)1 << 30) return NA3D_ERR_SHAPE;
-  if ((int64_t)B * T * H * W * NH * HD > ((int64_t)1 << 62) / 2) return NA3D_ERR_SHAPE;
-  if (H > (1 << 20) || W > (1 << 20)) return NA3D_ERR_SHAPE;
-  if (KT < 1 || KH < 1 || KW < 1 || KT > T || KH > H || KW > W) return NA3D_ERR_WINDOW;
-  return NA3D_OK;
-}
 
 template <int HD>
-int launch(const Args& a, const Plan& p, hipStream_t stream) {
-  auto kern = na3d_fwd_plane_kernel<HD, kQH, kQW, kWH, kWW>;
-  static std::atomic<int> attr_done{0};
-  if (!attr_done.load(std::memory_order_acquire)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kMaxLdsBytes) != hipSuccess)
-      return NA3D_ERR_LAUNCH;
-    attr_done.store(1, std::memory_order_release);
-  }
-  hipLaunchKernelGGL(kern, dim3((unsigned)p.wgs), dim3(p.threads), p.lds_bytes, stream, a);
-  return hipGetLastError() == hipSuccess ? NA3D_OK : NA3D_ERR_LAUNCH;
-}
-
-// gfx950 check, cached per device (0 unknown, 1 yes, -1 no)
-std::atomic<int> g_arch_ok[64];
-
-int device_ok() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return NA3D_ERR_DEVICE;
-  if (dev < 0 || dev >= 64) return NA3D_ERR_DEVICE;
-  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
-  if (st == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NA3D_ERR_DEVICE;
-    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
-    g_arch_ok[dev].store(st, std::memory_order_relaxed);
-  }
-  return st == 1 ? NA3D_OK : NA3D_ERR_DEVICE;
+int launch_hd(const GeneralArgs& a, const Launch& l, hipStream_t stream) {
+  auto kern = na3d_fwd_general_kernel<HD, kQH, kQW, kWH, kWW>;
+  if (l.lds_bytes > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, l.lds_bytes) != hipSuccess)
+    return -1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)l.wgs), dim3(l.threads), l.lds_bytes, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace
 
-extern "C" {
+int general_tile_h() { return kWH * kQH; }
+int general_tile_w() { return kWW * kQW; }
+int general_threads() { return kWave * kWH * kWW; }
+int general_row_bytes(int hd) { return hd * 2 + kLdsPad; }
 
-int na3d_abi_version(void) { return 1; }
-
-const char* na3d_status_string(int status) {
-  switch (status) {
-    case NA3D_OK: return "ok";
-    case NA3D_ERR_NULL: return "a tensor pointer is NULL";
-    case NA3D_ERR_SHAPE: return "a dimension is < 1 or the tensor is too large";
-    case NA3D_ERR_WINDOW: return "a window extent is < 1 or larger than its grid axis";
-    case NA3D_ERR_HEAD_DIM: return "head dimension must be 16, 32, 64, 128 or 256";
-    case NA3D_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-    case NA3D_ERR_OVERLAP: return "out overlaps q, k or v";
-    case NA3D_ERR_DEVICE: return "the current HIP device is not gfx950";
-    case NA3D_ERR_LAUNCH: return "the kernel launch failed";
-    default: return "unknown status";
+int launch_general(const Problem& p, const Launch& l, int hd, hipStream_t s) {
+  GeneralArgs a;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o;
+  a.B = p.B; a.T = p.T; a.H = p.H; a.W = p.W; a.NH = p.NH;
+  a.KT = p.KT; a.KH = p.KH; a.KW = p.KW;
+  a.tiles_h = l.tiles_h;
+  a.tiles_w = l.tiles_w;
+  a.lds_rows = l.lds_rows;
+  switch (hd) {
+    case 16: return launch_hd<16>(a, l, s);
+    case 32: return launch_hd<32>(a, l, s);
+    case 64: return launch_hd<64>(a, l, s);
+    case 128: return launch_hd<128>(a, l, s);
+    case 256: return launch_hd<256>(a, l, s);
+    default: return -1;
   }
 }
 
-int na3d_check_args(const void* q, const void* k, const void* v, const void* out, int B,
-                    int T, int H, int W, int NH, int HD, int KT, int KH, int KW) {
-  if (!q || !k || !v || !out) return NA3D_ERR_NULL;
-  const int rc = check_sizes(B, T, H, W, NH, HD, KT, KH, KW);
-  if (rc != NA3D_OK) return rc;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return NA3D_ERR_ALIGN;
-  const size_t bytes = (size_t)B * T * H * W * NH * HD * 2;
-  if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
-    return NA3D_ERR_OVERLAP;
-  return NA3D_OK;
-}
-
-int na3d_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, int* plan) {
-  if (!plan) return NA3D_ERR_NULL;
-  const int rc = check_sizes(B, T, H, W, NH, HD, KT, KH, KW);
-  if (rc != NA3D_OK) return rc;
-  Plan p;
-  const int rp = make_plan(B, T, H, W, NH, HD, KT, KH, KW, &p);
-  if (rp != NA3D_OK) return rp;
-  plan[0] = p.family;
-  plan[1] = p.bt;
-  plan[2] = p.bh;
-  plan[3] = p.bw;
-  plan[4] = (int)p.wgs;
-  plan[5] = p.threads;
-  plan[6] = p.lds_bytes;
-  plan[7] = p.planes;
-  return NA3D_OK;
-}
-
-int na3d_fwd(const void* q, const void* k, const void* v, void* out, int B, int T, int H,
-             int W, int NH, int HD, int KT, int KH, int KW, void* stream) {
-  int rc = na3d_check_args(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW);
-  if (rc != NA3D_OK) return rc;
-  Plan p;
-  rc = make_plan(B, T, H, W, NH, HD, KT, KH, KW, &p);
-  if (rc != NA3D_OK) return rc;
-  rc = device_ok();
-  if (rc != NA3D_OK) return rc;
-  Args a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = static_cast<uint16_t*>(out);
-  a.B = B; a.T = T; a.H = H; a.W = W; a.NH = NH;
-  a.KT = KT; a.KH = KH; a.KW = KW;
-  a.tiles_h = p.tiles_h;
-  a.tiles_w = p.tiles_w;
-  a.lds_rows = p.lds_rows;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (HD) {
-    case 16: return launch<16>(a, p, s);
-    case 32: return launch<32>(a, p, s);
-    case 64: return launch<64>(a, p, s);
-    case 128: return launch<128>(a, p, s);
-    case 256: return launch<256>(a, p, s);
-    default: return NA3D_ERR_HEAD_DIM;
-  }
-}
-
-}  // extern "C"
+}  // namespace na3d

@@ -1,0 +1,288 @@
+// na3d.cpp -- C ABI of the NA3D forward library: argument checks, launch
+// planning (which kernel family and instantiation runs a given shape) and
+// dispatch.  All checks run on the host before any device call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/na3d.h"
+#include "common.h"
+
+namespace na3d {
+
+int general_tile_h();
+int general_tile_w();
+int general_threads();
+int general_row_bytes(int hd);
+
+namespace {
+
+constexpr int kMaxLdsBytes = 160 * 1024;     // LDS of one CU
+constexpr int kGeneralLdsBytes = 80 * 1024;  // two general workgroups per CU
+constexpr int kTargetWorkgroups = 1024;      // 256 CUs x 4
+
+bool head_dim_ok(int hd) { return hd == 16 || hd == 32 || hd == 64 || hd == 128 || hd == 256; }
+
+bool overlaps(const void* a, const void* b, size_t bytes) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + bytes && y < x + bytes;
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+int check_sizes(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW) {
+  if (B < 1 || T < 1 || H < 1 || W < 1 || NH < 1 || HD < 1) return NA3D_ERR_SHAPE;
+  if (!head_dim_ok(HD)) return NA3D_ERR_HEAD_DIM;
+  // per-plane and per-batch element counts stay addressable in 32/64 bit
+  if ((int64_t)T * H * W > ((int64_t)1 << 30)) return NA3D_ERR_SHAPE;
+  if ((int64_t)B * T * H * W * NH * HD > ((int64_t)1 << 61)) return NA3D_ERR_SHAPE;
+  if (KT < 1 || KH < 1 || KW < 1 || KT > T || KH > H || KW > W) return NA3D_ERR_WINDOW;
+  return NA3D_OK;
+}
+
+// Most query planes one wave holds at a time: a run [t0, t0 + tc) is split
+// over WT waves (wave r owns t0 + r, t0 + r + WT, ...); count, over all key
+// planes, the owned query planes whose window contains that key plane.
+int max_active_per_wave(int T, int KT, int tc, int wt) {
+  int best = 0;
+  for (int t0 = 0; t0 < T; t0 += tc) {
+    const int t1 = std::min(t0 + tc, T);
+    const int p0 = win_start(t0, KT, T), p1 = win_start(t1 - 1, KT, T) + KT;
+    for (int r = 0; r < wt; ++r)
+      for (int tp = p0; tp < p1; ++tp) {
+        int c = 0;
+        for (int t = t0 + r; t < t1; t += wt) {
+          const int s = win_start(t, KT, T);
+          c += (s <= tp && tp < s + KT);
+        }
+        best = std::max(best, c);
+      }
+  }
+  return best;
+}
+
+bool plan_general(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, Launch* l) {
+  const int BH = general_tile_h(), BW = general_tile_w();
+  l->family = 1;
+  l->variant = 0;
+  l->tile_t = 1;
+  l->tile_h = BH;
+  l->tile_w = BW;
+  l->tiles_t = T;
+  l->tiles_h = ceil_div(H, BH);
+  l->tiles_w = ceil_div(W, BW);
+  l->wgs = (int64_t)B * NH * T * l->tiles_h * l->tiles_w;
+  l->threads = general_threads();
+  const int row = general_row_bytes(HD);
+  const int max_halo = std::min(BH + KH - 1, H) * std::min(BW + KW - 1, W);
+  l->lds_rows = std::min(max_halo, kGeneralLdsBytes / (2 * row));
+  l->lds_bytes = 2 * l->lds_rows * row;
+  l->planes = KT;
+  (void)KW;
+  return l->wgs <= 0x7fffffff;
+}
+
+// Can rolling variant v run these sizes?  tile_t = 0 picks the run length.
+bool plan_roll(int v, int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
+               int tile_t, Launch* l) {
+  if (v < 0 || v >= kNumRollVariants) return false;
+  const RollVariant& rv = kRollVariants[v];
+  if (rv.hd != HD) return false;
+  const int BH = rv.wh * rv.qh;
+  const int hwd_max = std::min(rv.qw + KW - 1, W);
+  const int un_max = std::min(rv.qh + KH - 1, H) * hwd_max;
+  if (un_max / 32 > rv.maxb) return false;
+  const int halo_max = std::min(BH + KH - 1, H) * hwd_max;
+  // K and V rows of HD*2 bytes, in one or two plane buffers
+  const int64_t lds = 2LL * rv.nbuf * halo_max * (HD * 2);
+  if (lds > kMaxLdsBytes) return false;
+  const int tiles_h = ceil_div(H, BH), tiles_w = ceil_div(W, rv.qw);
+  const int64_t spatial = (int64_t)B * NH * tiles_h * tiles_w;
+  int tc;
+  if (tile_t > 0) {
+    tc = std::min(tile_t, T);
+    if (max_active_per_wave(T, KT, tc, rv.wt) > rv.ns) return false;
+  } else {
+    // longest run that fits the slots, shortened while the grid is too small
+    tc = T;
+    while (tc > 1 && max_active_per_wave(T, KT, tc, rv.wt) > rv.ns) --tc;
+    if (max_active_per_wave(T, KT, tc, rv.wt) > rv.ns) return false;
+    while (tc > rv.wt && spatial * ceil_div(T, tc) < kTargetWorkgroups) tc = ceil_div(tc, 2);
+  }
+  l->family = 2;
+  l->variant = v;
+  l->tile_t = tc;
+  l->tile_h = BH;
+  l->tile_w = rv.qw;
+  l->tiles_t = ceil_div(T, tc);
+  l->tiles_h = tiles_h;
+  l->tiles_w = tiles_w;
+  l->wgs = spatial * l->tiles_t;
+  l->threads = kWave * rv.wh * rv.wt;
+  l->lds_rows = halo_max;
+  l->lds_bytes = (int)lds;
+  l->planes = std::min(T, win_start(std::min(tc, T) - 1, KT, T) + KT);
+  return l->wgs <= 0x7fffffff;
+}
+
+// Preferred rolling instantiations, best first, by head dimension and window
+// area (large windows need big unions and favour single-buffered staging).
+int pick_roll(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, Launch* l) {
+  static const int p16[] = {0};
+  static const int p32[] = {1};
+  static const int p64_small[] = {2, 3, 4, 8, 6};
+  static const int p64_large[] = {8, 6, 7};
+  static const int p128[] = {9, 10, 11};
+  static const int p256[] = {12};
+  const int* pref;
+  int np;
+  switch (HD) {
+    case 16: pref = p16; np = 1; break;
+    case 32: pref = p32; np = 1; break;
+    case 64:
+      if (KH * KW <= 64) { pref = p64_small; np = 5; } else { pref = p64_large; np = 3; }
+      break;
+    case 128: pref = p128; np = 3; break;
+    default: pref = p256; np = 1; break;
+  }
+  for (int i = 0; i < np; ++i)
+    if (plan_roll(pref[i], B, T, H, W, NH, HD, KT, KH, KW, 0, l)) return 1;
+  return 0;
+}
+
+int make_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, Launch* l) {
+  if (pick_roll(B, T, H, W, NH, HD, KT, KH, KW, l)) return NA3D_OK;
+  if (plan_general(B, T, H, W, NH, HD, KT, KH, KW, l)) return NA3D_OK;
+  return NA3D_ERR_SHAPE;
+}
+
+int make_plan_config(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
+                     int family, int variant, int tile_t, Launch* l) {
+  if (family == 0) return make_plan(B, T, H, W, NH, HD, KT, KH, KW, l);
+  if (family == 1)
+    return plan_general(B, T, H, W, NH, HD, KT, KH, KW, l) ? NA3D_OK : NA3D_ERR_SHAPE;
+  if (family == 2)
+    return plan_roll(variant, B, T, H, W, NH, HD, KT, KH, KW, tile_t, l) ? NA3D_OK
+                                                                          : NA3D_ERR_CONFIG;
+  return NA3D_ERR_CONFIG;
+}
+
+void fill_plan(const Launch& l, int* plan) {
+  plan[0] = l.family;
+  plan[1] = l.tile_t;
+  plan[2] = l.tile_h;
+  plan[3] = l.tile_w;
+  plan[4] = (int)l.wgs;
+  plan[5] = l.threads;
+  plan[6] = l.lds_bytes;
+  plan[7] = l.planes;
+}
+
+// gfx950 check, cached per device (0 unknown, 1 yes, -1 no)
+std::atomic<int> g_arch_ok[64];
+
+int device_ok() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NA3D_ERR_DEVICE;
+  if (dev < 0 || dev >= 64) return NA3D_ERR_DEVICE;
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NA3D_ERR_DEVICE;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? NA3D_OK : NA3D_ERR_DEVICE;
+}
+
+int run(const void* q, const void* k, const void* v, void* out, int B, int T, int H, int W,
+        int NH, int HD, int KT, int KH, int KW, const Launch& l, void* stream) {
+  int rc = device_ok();
+  if (rc != NA3D_OK) return rc;
+  Problem p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(out);
+  p.B = B; p.T = T; p.H = H; p.W = W; p.NH = NH;
+  p.KT = KT; p.KH = KH; p.KW = KW;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = l.family == 2 ? launch_roll(p, l, HD, s) : launch_general(p, l, HD, s);
+  return rc == 0 ? NA3D_OK : NA3D_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace na3d
+
+using namespace na3d;
+
+extern "C" {
+
+int na3d_abi_version(void) { return 1; }
+
+int na3d_num_variants(void) { return kNumRollVariants; }
+
+const char* na3d_status_string(int status) {
+  switch (status) {
+    case NA3D_OK: return "ok";
+    case NA3D_ERR_NULL: return "a tensor pointer is NULL";
+    case NA3D_ERR_SHAPE: return "a dimension is < 1 or the tensor is too large";
+    case NA3D_ERR_WINDOW: return "a window extent is < 1 or larger than its grid axis";
+    case NA3D_ERR_HEAD_DIM: return "head dimension must be 16, 32, 64, 128 or 256";
+    case NA3D_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case NA3D_ERR_OVERLAP: return "out overlaps q, k or v";
+    case NA3D_ERR_DEVICE: return "the current HIP device is not gfx950";
+    case NA3D_ERR_LAUNCH: return "the kernel launch failed";
+    case NA3D_ERR_CONFIG: return "the requested launch configuration cannot run these sizes";
+    default: return "unknown status";
+  }
+}
+
+int na3d_check_args(const void* q, const void* k, const void* v, const void* out, int B,
+                    int T, int H, int W, int NH, int HD, int KT, int KH, int KW) {
+  if (!q || !k || !v || !out) return NA3D_ERR_NULL;
+  const int rc = check_sizes(B, T, H, W, NH, HD, KT, KH, KW);
+  if (rc != NA3D_OK) return rc;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return NA3D_ERR_ALIGN;
+  const size_t bytes = (size_t)B * T * H * W * NH * HD * 2;
+  if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
+    return NA3D_ERR_OVERLAP;
+  return NA3D_OK;
+}
+
+int na3d_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, int* plan) {
+  return na3d_plan_config(B, T, H, W, NH, HD, KT, KH, KW, 0, 0, 0, plan);
+}
+
+int na3d_plan_config(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
+                     int family, int variant, int tile_t, int* plan) {
+  if (!plan) return NA3D_ERR_NULL;
+  int rc = check_sizes(B, T, H, W, NH, HD, KT, KH, KW);
+  if (rc != NA3D_OK) return rc;
+  Launch l;
+  rc = make_plan_config(B, T, H, W, NH, HD, KT, KH, KW, family, variant, tile_t, &l);
+  if (rc != NA3D_OK) return rc;
+  fill_plan(l, plan);
+  return NA3D_OK;
+}
+
+int na3d_fwd(const void* q, const void* k, const void* v, void* out, int B, int T, int H,
+             int W, int NH, int HD, int KT, int KH, int KW, void* stream) {
+  return na3d_fwd_config(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW, 0, 0, 0, stream);
+}
+
+int na3d_fwd_config(const void* q, const void* k, const void* v, void* out, int B, int T,
+                    int H, int W, int NH, int HD, int KT, int KH, int KW, int family,
+                    int variant, int tile_t, void* stream) {
+  int rc = na3d_check_args(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW);
+  if (rc != NA3D_OK) return rc;
+  Launch l;
+  rc = make_plan_config(B, T, H, W, NH, HD, KT, KH, KW, family, variant, tile_t, &l);
+  if (rc != NA3D_OK) return rc;
+  return run(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW, l, stream);
+}
+
+}  // extern "C"

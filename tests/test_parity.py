@@ -199,3 +199,51 @@ def test_python_binding_rejects_bad_tensors():
         na.fwd(q, k[:, :1], v, (1, 3, 3))
     with pytest.raises(na.NA3DError):
         na.fwd(q, k, v, (3, 3, 3))  # KT > T
+
+
+# ------------------------------------------------------------ every instantiation
+def variant_cases():
+    """(family, variant, shape, window) for every compiled instantiation, on
+    shapes with border shifts, ragged tiles and several query planes."""
+    cases = []
+    for fam_shape in [((1, 9, 13, 21, 2, 64), (3, 7, 7)), ((1, 12, 20, 24, 2, 64), (11, 11, 11))]:
+        cases.append((1, 0) + fam_shape)
+    table = {16: ((1, 7, 11, 19, 2, 16), (3, 5, 5)), 32: ((1, 7, 11, 19, 2, 32), (3, 5, 7)),
+             64: ((2, 9, 13, 21, 2, 64), (3, 7, 7)), 128: ((1, 7, 11, 19, 2, 128), (3, 7, 7)),
+             256: ((1, 5, 9, 17, 1, 256), (3, 5, 5))}
+    big = ((1, 12, 18, 22, 2, 64), (11, 11, 11))
+    import ctypes
+    lib = na.load()
+    for var in range(na.num_variants()):
+        for hd, (shape, ks) in table.items():
+            buf = (ctypes.c_int * 8)()
+            if lib.na3d_plan_config(*shape, *ks, 2, var, 0, buf) == 0:
+                cases.append((2, var, shape, ks))
+        buf = (ctypes.c_int * 8)()
+        if lib.na3d_plan_config(*big[0], *big[1], 2, var, 0, buf) == 0:
+            cases.append((2, var) + big)
+    return cases
+
+
+@pytest.mark.parametrize("fam,var,shape,ks", variant_cases(),
+                         ids=lambda x: str(x).replace(" ", ""))
+def test_each_instantiation(fam, var, shape, ks):
+    print("case family=%d variant=%d shape=%s window=%s" % (fam, var, shape, ks), flush=True)
+    q, k, v = inputs_on_gpu(shape, 77 + var)
+    out = na.fwd(q, k, v, ks, config=(fam, var, 0))
+    torch.cuda.synchronize()
+    ref = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), ks)
+    compare(to_np(out), ref, "family %d variant %d" % (fam, var))
+
+
+@pytest.mark.parametrize("tile_t", [1, 2, 3, 5, 16])
+def test_rolling_run_lengths(tile_t):
+    """Query-plane runs of any length give the same result (admission and
+    retirement of query planes across run boundaries)."""
+    shape, ks = (1, 16, 10, 17, 2, 64), (3, 5, 5)
+    q, k, v = inputs_on_gpu(shape, 90)
+    p = na.plan(shape, ks)
+    assert p["family"] == 2
+    out = na.fwd(q, k, v, ks, config=(2, 2, tile_t))
+    torch.cuda.synchronize()
+    compare(to_np(out), oracle.fwd(q.cpu(), k.cpu(), v.cpu(), ks), "run length %d" % tile_t)
