@@ -22,16 +22,30 @@ constexpr float kLog2e = 1.4426950408889634f;
 // bytes = HD/8 chunks of 16 bytes; logical chunk c of row r is stored at
 // physical chunk c ^ swz(r).  swz depends only on r mod 16, and the operand
 // reads of a 32-key block start at multiples of 16 rows, so the XOR term is a
-// per-lane constant.  The function is chosen so that both operand reads are
-// free of LDS bank conflicts (64 banks of 4 bytes):
-//   K read  -- 16 lanes take the same logical chunk of 16 consecutive rows;
-//   V read  -- the transpose read takes 8 bytes from each of 4 consecutive
-//              rows per 4 lanes, i.e. one 32-byte chunk pair per row.
+// per-lane constant.
+//
+// Measured on gfx950 (bank-conflict counters over probe patterns): a 16-byte
+// LDS read is served 32 lanes at a time against 128 banks of 4 bytes, the
+// 8-byte transpose read 32 lanes at a time against 64 banks.  The K operand
+// read puts 16 rows x 2 chunks in one pass, the V operand (transpose) read 8
+// rows x 32 bytes.  With the key order of key_perm below, swz makes both
+// passes hit distinct banks: for every row offset when HD = 16, 64 or 256,
+// for even row offsets when HD = 128 (the usual case: halo widths are even),
+// and the V read stays 2-way when HD = 32.
 __host__ __device__ constexpr int swz(int hd, int r) {
-  return hd == 16   ? (r >> 3) & 1
-         : hd == 32 ? (r >> 2) & 3
-         : hd == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))
-                    : ((r & 7) << 1) | ((r >> 3) & 1);
+  return hd == 16    ? (r >> 3) & 1
+         : hd == 32  ? (r >> 2) & 3
+         : hd == 64  ? ((r >> 2) & 3) << 1
+         : hd == 128 ? ((((r >> 1) + 4 * (r & 1)) & 7) << 1)
+                     : (r & 15) << 1;
+}
+
+// Which key of a 16-key tile feeds MFMA row/column m.  Any permutation is
+// valid as long as the K rows, the V rows and the window mask agree on it;
+// for HD = 64 a 4 x 4 transpose makes the V read touch rows 4 apart, which is
+// what lets swz serve both operand reads without conflicts.
+__host__ __device__ constexpr int key_perm(int hd, int m) {
+  return hd == 64 ? 4 * (m & 3) + (m >> 2) : m;
 }
 
 // Inward-shifted window start on one axis: clamp(i - K/2, 0, L - K).
@@ -76,29 +90,33 @@ struct Launch {
 // Instantiations of the rolling family: index, head dim, query block
 // (QH x QW = 16), wave grid (WH block rows x WT query-plane phases), query-plane
 // slots per wave, the most full 32-key blocks a wave's window union may hold,
-// and the number of staged plane buffers.
-#define NA3D_ROLL_VARIANTS(X)          \
-  X(0, 16, 2, 8, 2, 2, 2, 4, 2)        \
-  X(1, 32, 2, 8, 2, 2, 2, 4, 2)        \
-  X(2, 64, 2, 8, 2, 2, 2, 4, 2)        \
-  X(3, 64, 2, 8, 2, 2, 2, 4, 1)        \
-  X(4, 64, 2, 8, 4, 1, 4, 4, 2)        \
-  X(5, 64, 2, 8, 1, 4, 2, 4, 2)        \
-  X(6, 64, 4, 4, 1, 4, 4, 7, 1)        \
-  X(7, 64, 4, 4, 2, 2, 4, 7, 1)        \
-  X(8, 64, 4, 4, 1, 8, 2, 7, 1)        \
-  X(9, 128, 2, 8, 2, 2, 2, 4, 1)       \
-  X(10, 128, 2, 8, 2, 2, 2, 4, 2)      \
-  X(11, 128, 2, 8, 1, 4, 2, 4, 1)      \
-  X(12, 256, 2, 8, 1, 2, 2, 4, 1)
+// the number of staged plane buffers, and the blocks per softmax group.
+#define NA3D_ROLL_VARIANTS(X)             \
+  X(0, 16, 2, 8, 1, 4, 1, 4, 2, 5)        \
+  X(1, 32, 2, 8, 1, 4, 1, 4, 2, 5)        \
+  X(2, 64, 2, 8, 1, 4, 1, 4, 2, 5)        \
+  X(3, 64, 2, 8, 2, 4, 1, 4, 1, 5)        \
+  X(4, 64, 2, 8, 1, 4, 1, 4, 1, 5)        \
+  X(5, 64, 2, 8, 2, 2, 2, 4, 2, 5)        \
+  X(6, 64, 4, 4, 1, 8, 2, 7, 1, 4)        \
+  X(7, 64, 4, 4, 1, 8, 2, 7, 1, 2)        \
+  X(8, 64, 4, 4, 1, 4, 4, 7, 1, 2)        \
+  X(9, 128, 2, 8, 1, 4, 1, 4, 1, 5)       \
+  X(10, 128, 2, 8, 1, 4, 1, 4, 2, 5)      \
+  X(11, 128, 2, 8, 2, 2, 2, 4, 1, 5)      \
+  X(12, 256, 2, 8, 1, 4, 1, 4, 1, 5)
+
+// Zeroed rows past the staged halo in each rolling plane buffer: the union's
+// partial last block reads at most 15 rows past the halo.
+constexpr int kPadRows = 16;
 
 struct RollVariant {
-  int hd, qh, qw, wh, wt, ns, maxb, nbuf;
+  int hd, qh, qw, wh, wt, ns, maxb, nbuf, sb;
 };
 
 constexpr RollVariant kRollVariants[] = {
-#define NA3D_ROLL_ENTRY(i, HD, QH, QW, WH, WT, NS, MAXB, NBUF) \
-  {HD, QH, QW, WH, WT, NS, MAXB, NBUF},
+#define NA3D_ROLL_ENTRY(i, HD, QH, QW, WH, WT, NS, MAXB, NBUF, SB) \
+  {HD, QH, QW, WH, WT, NS, MAXB, NBUF, SB},
     NA3D_ROLL_VARIANTS(NA3D_ROLL_ENTRY)
 #undef NA3D_ROLL_ENTRY
 };

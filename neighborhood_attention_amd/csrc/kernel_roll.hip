@@ -23,25 +23,29 @@
 // window start and retired, output written, after its last key plane), and
 // reuses every K/V fragment it reads from LDS for all of them.
 //
-// Per 32-key block of a wave's union, for all active query planes at once:
+// Within a 16-key tile the keys feed the MFMA rows in the order key_perm
+// (chosen for conflict-free LDS reads); K rows, V rows and window masks all
+// use that order.
+//
+// Per key plane, a wave walks its union in groups of up to SB 32-key blocks;
+// each group runs three phases, each over all of its blocks and all active
+// query planes, so the MFMAs and exponentials of a phase are independent:
 //   S^T = K . Q^T + bias    bf16 MFMA 16x16x32; bias (0 or -inf) is the
 //                           window mask, computed once per wave and fed in
 //                           as the accumulator input, so masking costs no VALU
-//   lazy online softmax     the running max is refreshed only when a score
-//                           exceeds it by more than kRescale (one ballot)
+//   softmax                 one exact max over the group's scores, one
+//                           rescale of the running output, then exp2
 //   O^T += V^T . P^T        bf16 MFMA; the S^T accumulator layout is already
 //                           the P^T operand, V^T comes from the transpose read
-// The phases run over all active query planes in turn, so independent MFMAs
-// and softmax chains interleave.  The union's last partial block uses a
-// 16-key step (MFMA 16x16x16) when it holds at most 16 keys.
+// The union's last partial block uses a 16-key step (MFMA 16x16x16) when it
+// holds at most 16 keys.  Its masked keys read staged rows past the union;
+// each plane buffer carries kPadRows zeroed rows past the halo, so such rows
+// always hold finite values (which the -inf bias then removes).
 #include "common.h"
 
 namespace na3d {
 namespace {
 
-// Natural-log headroom before the reference max is refreshed: unnormalised
-// weights stay below e^5.5 (about 245), far inside fp32 and bf16 range.
-constexpr float kRescale = 5.5f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr uint32_t kBf16NegInf = 0xff80u;
 
@@ -63,8 +67,7 @@ struct Slot {
   static constexpr int MT = HD / 16;
   bf16x8 qf[KSTEPS];  // Q^T operand: lane (q16, g) holds head dims [32ks + 8g, +8)
   f32x4 acc[MT];      // O^T: lane (q16, g) holds head dims 16mt + 4g + r
-  float m;            // reference max (natural units), -inf before any key
-  float mb;           // m * log2(e), 0 while m is -inf
+  float m;            // running max (natural units), -inf before any key
   float l;            // this lane's share of the softmax denominator
 };
 
@@ -82,7 +85,6 @@ __device__ __forceinline__ void reset_state(Slot<HD>& S) {
 #pragma unroll
   for (int mt = 0; mt < Slot<HD>::MT; ++mt) S.acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   S.m = kNegInf;
-  S.mb = 0.f;
   S.l = 0.f;
 }
 
@@ -101,37 +103,6 @@ __device__ __forceinline__ void slot_finish(Slot<HD>& S, uint16_t* op, int g, bo
           make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
     }
   }
-}
-
-// Refresh the reference max of a query plane when one of its scores exceeds
-// it by more than kRescale; bm is this lane's block maximum.
-template <int HD>
-__device__ __forceinline__ void maybe_rescale(Slot<HD>& S, float bm) {
-  if (__builtin_amdgcn_ballot_w64(bm > S.m + kRescale) == 0) return;
-  float qm = fmaxf(bm, __shfl_xor(bm, 16));
-  qm = fmaxf(qm, __shfl_xor(qm, 32));
-  const float mn = fmaxf(S.m, qm);
-  const float alpha = S.m == kNegInf ? 0.f : __builtin_amdgcn_exp2f((S.m - mn) * kLog2e);
-#pragma unroll
-  for (int mt = 0; mt < Slot<HD>::MT; ++mt) S.acc[mt] *= alpha;
-  S.l *= alpha;
-  S.m = mn;
-  S.mb = mn == kNegInf ? 0.f : mn * kLog2e;
-}
-
-// Softmax of one score group: p = exp2(s*log2e - m*log2e), running sum.
-template <int HD, int N>
-__device__ __forceinline__ void softmax_block(Slot<HD>& S, const float (&s)[N], float (&p)[N]) {
-  float bm = s[0];
-#pragma unroll
-  for (int j = 1; j < N; ++j) bm = fmaxf(bm, s[j]);
-  maybe_rescale(S, bm);
-#pragma unroll
-  for (int j = 0; j < N; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], kLog2e, -S.mb));
-  float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < N; ++j) sum += p[j];
-  S.l += sum;
 }
 
 // V^T operand through the transpose read: lane (4j + a) of a 16-lane group
@@ -167,79 +138,9 @@ __device__ __forceinline__ void unpack_bias(const uint32_t (&w)[4], f32x4& b0, f
              __builtin_bit_cast(float, w[3] << 16), __builtin_bit_cast(float, w[3] & 0xffff0000u)};
 }
 
-// One 32-key block for all active query planes of the wave.
-template <int HD, int NS>
-__device__ __forceinline__ void block32(Slot<HD> (&S)[NS], const bool (&sact)[NS],
-                                        const bf16x8 (&kf)[2][Slot<HD>::KSTEPS],
-                                        const bf16x8 (&vf)[Slot<HD>::MT], const f32x4& b0,
-                                        const f32x4& b1) {
-  f32x4 sc[NS][2];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    sc[s][0] = b0;
-    sc[s][1] = b1;
-    if (!sact[s]) continue;
-#pragma unroll
-    for (int ks = 0; ks < Slot<HD>::KSTEPS; ++ks) {
-      sc[s][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][ks], S[s].qf[ks], sc[s][0], 0, 0, 0);
-      sc[s][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][ks], S[s].qf[ks], sc[s][1], 0, 0, 0);
-    }
-  }
-  bf16x8 pf[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (!sact[s]) continue;
-    const float sv[8] = {sc[s][0][0], sc[s][0][1], sc[s][0][2], sc[s][0][3],
-                         sc[s][1][0], sc[s][1][1], sc[s][1][2], sc[s][1][3]};
-    float p[8];
-    softmax_block<HD, 8>(S[s], sv, p);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pf[s][j] = (__bf16)p[j];
-  }
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (!sact[s]) continue;
-#pragma unroll
-    for (int mt = 0; mt < Slot<HD>::MT; ++mt)
-      S[s].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[mt], pf[s], S[s].acc[mt], 0, 0, 0);
-  }
-}
-
-// One 16-key block (the union's tail) for all active query planes.
-template <int HD, int NS>
-__device__ __forceinline__ void block16(Slot<HD> (&S)[NS], const bool (&sact)[NS],
-                                        const bf16x8 (&kf)[Slot<HD>::KSTEPS],
-                                        const s16x4 (&vf)[Slot<HD>::MT], const f32x4& b0) {
-  f32x4 sc[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    sc[s] = b0;
-    if (!sact[s]) continue;
-#pragma unroll
-    for (int ks = 0; ks < Slot<HD>::KSTEPS; ++ks)
-      sc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], S[s].qf[ks], sc[s], 0, 0, 0);
-  }
-  s16x4 pf[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (!sact[s]) continue;
-    const float sv[4] = {sc[s][0], sc[s][1], sc[s][2], sc[s][3]};
-    float p[4];
-    softmax_block<HD, 4>(S[s], sv, p);
-    const bf16x4 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
-    pf[s] = __builtin_bit_cast(s16x4, pb);
-  }
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (!sact[s]) continue;
-#pragma unroll
-    for (int mt = 0; mt < Slot<HD>::MT; ++mt)
-      S[s].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[mt], pf[s], S[s].acc[mt], 0, 0, 0);
-  }
-}
-
-template <int HD, int QH, int QW, int WH, int WT, int NS, int MAXB, int NBUF>
+template <int HD, int QH, int QW, int WH, int WT, int NS, int MAXB, int NBUF, int SB>
 __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const RollArgs a) {
+  constexpr int NGRP = (MAXB + 1 + SB - 1) / SB;  // groups covering MAXB full blocks + a tail
   static_assert(QH * QW == 16, "a wave owns 16 queries");
   static_assert(NBUF == 1 || NBUF == 2, "one or two plane buffers");
   constexpr int KSTEPS = Slot<HD>::KSTEPS;
@@ -301,8 +202,7 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
   const int uh0 = bh0 < H ? win_start(bh0, KH, H) : hh0;
   const int un = active ? (win_start(bh1, KH, H) + KH - uh0) * hwd : 0;
   const int base = (uh0 - hh0) * hwd;
-  const int nmain = un >> 5;  // full 32-key blocks
-  const int rem = un & 31;    // keys in the tail block
+  const int nblk = (un + 31) >> 5;  // 32-key blocks, the last possibly partial
 
   // ---- window masks, packed as bf16 pairs (0 = in window, -inf = out)
   const float inv_hwd = 1.f / (float)hwd;
@@ -319,28 +219,27 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
   auto bias_words = [&](int u0, uint32_t (&w)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int u = u0 + 16 * (i >> 1) + 4 * g + 2 * (i & 1);
-      w[i] = key_out(u) | (key_out(u + 1) << 16);
+      // score slot r of tile ct holds key 16ct + key_perm(4g + r)
+      const int r = 2 * (i & 1);
+      const int u = u0 + 16 * (i >> 1);
+      w[i] = key_out(u + key_perm(HD, 4 * g + r)) | (key_out(u + key_perm(HD, 4 * g + r + 1)) << 16);
     }
   };
-  uint32_t bias[MAXB][4];
+  uint32_t bias[MAXB + 1][4];  // MAXB full blocks and the tail
 #pragma unroll
-  for (int bb = 0; bb < MAXB; ++bb) bias_words(32 * bb, bias[bb]);
-  uint32_t tbias[4];
-  bias_words(32 * nmain, tbias);
+  for (int bb = 0; bb <= MAXB; ++bb) bias_words(32 * bb, bias[bb]);
 
   // ---- operand offsets inside one plane buffer; blocks add multiples of 16
   // rows, which leave the swizzle unchanged
+  // K operand: lane (q16, g) holds key kp of a tile; V operand (transpose
+  // read): lane (4j + a) of group g addresses key vp = key_perm(4g + j)
+  const int kp = key_perm(HD, q16);
+  const int vp = key_perm(HD, 4 * g + (q16 >> 2));
   int kofs[KSTEPS], vofs[MT];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) kofs[ks] = k_addr<HD>(base + q16, 4 * ks + g);
+  for (int ks = 0; ks < KSTEPS; ++ks) kofs[ks] = k_addr<HD>(base + kp, 4 * ks + g);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) vofs[mt] = v_addr<HD>(base + 4 * g + (q16 >> 2), mt, q16);
-  const int last = max(un - 1, 0);
-  const int tb = 32 * nmain;
-  const int tk0 = base + min(tb + q16, last), tk1 = base + min(tb + 16 + q16, last);
-  const int tv0 = base + min(tb + 4 * g + (q16 >> 2), last);
-  const int tv1 = base + min(tb + 16 + 4 * g + (q16 >> 2), last);
+  for (int mt = 0; mt < MT; ++mt) vofs[mt] = v_addr<HD>(base + vp, mt, q16);
 
   const int64_t tok = (int64_t)a.NH * HD;
   const int64_t plane = (int64_t)H * W * tok;
@@ -377,6 +276,16 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
   unsigned preloaded = 0;  // slots whose Q was fetched one plane early
   int jlo = 0, jhi = -1;   // query planes j in [jlo, jhi] are in flight
   const int p0 = win_start(t0, KT, T), p1 = win_start(t1 - 1, KT, T) + KT;
+  // zero the rows past the halo in every buffer (never staged; read only by
+  // masked tail keys); the first barrier of the stream orders these stores
+  {
+    const int pad16 = (a.lds_rows - halo_rows) * (RB / 16);
+    for (int i = tid; i < 2 * NBUF * pad16; i += NT) {
+      const int region = i / pad16;
+      *reinterpret_cast<uint4*>(smem + region * buf_bytes + halo_rows * RB + (i - region * pad16) * 16) =
+          make_uint4(0, 0, 0, 0);
+    }
+  }
   issue_stage(p0, NBUF == 2 ? (p0 & 1) : 0);  // key plane tp lives in buffer tp % NBUF
   for (int tp = p0; tp < p1; ++tp) {
     // admit this wave's query planes whose window starts here
@@ -413,54 +322,119 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
       bool sact[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) sact[s] = ((s - jlo % NS + NS) % NS) < (jhi - jlo + 1);
-
+      // The union is processed in groups of SB 32-key blocks; each group runs
+      // three phases over all of its blocks and all active query planes:
+      // scores, softmax (one exact group max, one rescale), P.V.
 #pragma unroll
-      for (int bb = 0; bb < MAXB; ++bb) {
-        if (bb < nmain) {
+      for (int grp = 0; grp < NGRP; ++grp) {
+        if (grp * SB >= nblk) break;
+        f32x4 sc[NS][SB][2];
+        // ---- phase 1: S^T = K . Q^T + mask for every block of the group
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          const int bi = grp * SB + j;
+          if (bi > MAXB || bi >= nblk) break;
+          const bool half = 32 * bi + 16 >= un;  // a tail of at most 16 keys
           bf16x8 kf[2][KSTEPS];
 #pragma unroll
           for (int ks = 0; ks < KSTEPS; ++ks) {
             const bool use = 32 * ks + 8 * g < HD;
-            kf[0][ks] = use ? *reinterpret_cast<const bf16x8*>(lk + kofs[ks] + 32 * bb * RB) : bf16x8{};
-            kf[1][ks] = use ? *reinterpret_cast<const bf16x8*>(lk + kofs[ks] + (32 * bb + 16) * RB) : bf16x8{};
+            const unsigned char* ka = lk + kofs[ks] + 32 * bi * RB;
+            kf[0][ks] = use ? *reinterpret_cast<const bf16x8*>(ka) : bf16x8{};
+            kf[1][ks] = bf16x8{};
+            if (!half) kf[1][ks] = use ? *reinterpret_cast<const bf16x8*>(ka + 16 * RB) : bf16x8{};
           }
-          bf16x8 vf[MT];
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            vf[mt] = cat8(load_vt(lv, vofs[mt] + 32 * bb * RB),
-                          load_vt(lv, vofs[mt] + (32 * bb + 16) * RB));
           f32x4 b0, b1;
-          unpack_bias(bias[bb], b0, b1);
-          block32<HD, NS>(S, sact, kf, vf, b0, b1);
+          unpack_bias(bias[bi], b0, b1);
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            sc[s][j][0] = b0;
+            sc[s][j][1] = b1;
+            if (!sact[s]) continue;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+              sc[s][j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][ks], S[s].qf[ks], sc[s][j][0], 0, 0, 0);
+              if (!half)
+                sc[s][j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][ks], S[s].qf[ks], sc[s][j][1], 0, 0, 0);
+            }
+          }
         }
-      }
-      if (rem > 16) {
-        bf16x8 kf[2][KSTEPS];
+        // ---- phase 2: softmax over the group (the masked half of a 16-key
+        // tail block holds -inf and contributes nothing)
+        bf16x8 pf[NS][SB];
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const bool use = 32 * ks + 8 * g < HD;
-          kf[0][ks] = use ? *reinterpret_cast<const bf16x8*>(lk + k_addr<HD>(tk0, 4 * ks + g)) : bf16x8{};
-          kf[1][ks] = use ? *reinterpret_cast<const bf16x8*>(lk + k_addr<HD>(tk1, 4 * ks + g)) : bf16x8{};
+        for (int s = 0; s < NS; ++s) {
+          if (!sact[s]) continue;
+          float mx = kNegInf;
+#pragma unroll
+          for (int j = 0; j < SB; ++j) {
+            const int bi = grp * SB + j;
+            if (bi > MAXB || bi >= nblk) break;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fmaxf(sc[s][j][0][r], sc[s][j][1][r]));
+          }
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float mn = fmaxf(S[s].m, mx);
+          const float alpha = S[s].m == kNegInf ? 0.f : __builtin_amdgcn_exp2f((S[s].m - mn) * kLog2e);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) S[s].acc[mt] *= alpha;
+          S[s].m = mn;
+          const float mb = mn == kNegInf ? 0.f : mn * kLog2e;
+          float sum0 = 0.f, sum1 = 0.f;
+#pragma unroll
+          for (int j = 0; j < SB; ++j) {
+            const int bi = grp * SB + j;
+            if (bi > MAXB || bi >= nblk) break;
+            float p[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s][j][0][r], kLog2e, -mb));
+              p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s][j][1][r], kLog2e, -mb));
+            }
+            sum0 += (p[0] + p[1]) + (p[2] + p[3]);
+            sum1 += (p[4] + p[5]) + (p[6] + p[7]);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) pf[s][j][r] = (__bf16)p[r];
+          }
+          S[s].l = S[s].l * alpha + (sum0 + sum1);
         }
-        bf16x8 vf[MT];
+        // ---- phase 3: O^T += V^T . P^T for every block of the group
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          vf[mt] = cat8(load_vt(lv, v_addr<HD>(tv0, mt, q16)), load_vt(lv, v_addr<HD>(tv1, mt, q16)));
-        f32x4 b0, b1;
-        unpack_bias(tbias, b0, b1);
-        block32<HD, NS>(S, sact, kf, vf, b0, b1);
-      } else if (rem > 0) {
-        bf16x8 kf[KSTEPS];
+        for (int j = 0; j < SB; ++j) {
+          const int bi = grp * SB + j;
+          if (bi > MAXB || bi >= nblk) break;
+          const bool half = 32 * bi + 16 >= un;
+          if (half) {
+            s16x4 vf[MT];
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
-          kf[ks] = (32 * ks + 8 * g < HD) ? *reinterpret_cast<const bf16x8*>(lk + k_addr<HD>(tk0, 4 * ks + g))
-                                          : bf16x8{};
-        s16x4 vf[MT];
+            for (int mt = 0; mt < MT; ++mt) vf[mt] = load_vt(lv, vofs[mt] + 32 * bi * RB);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) vf[mt] = load_vt(lv, v_addr<HD>(tv0, mt, q16));
-        f32x4 b0, b1;
-        unpack_bias(tbias, b0, b1);
-        block16<HD, NS>(S, sact, kf, vf, b0);
+            for (int s = 0; s < NS; ++s) {
+              if (!sact[s]) continue;
+              const bf16x4 lo = {pf[s][j][0], pf[s][j][1], pf[s][j][2], pf[s][j][3]};
+              const s16x4 pb = __builtin_bit_cast(s16x4, lo);
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                S[s].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[mt], pb, S[s].acc[mt], 0, 0, 0);
+            }
+          } else {
+            bf16x8 vf[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              vf[mt] = cat8(load_vt(lv, vofs[mt] + 32 * bi * RB), load_vt(lv, vofs[mt] + (32 * bi + 16) * RB));
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              if (!sact[s]) continue;
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                S[s].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[mt], pf[s][j], S[s].acc[mt], 0, 0, 0);
+            }
+          }
+        }
+        // keep the scheduler from hoisting the next group's operand reads
+        // above this one, which would hold every group's fragments at once
+        if (NGRP > 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -484,9 +458,9 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
 }
 
 // ------------------------------------------------------------------ launch
-template <int HD, int QH, int QW, int WH, int WT, int NS, int MAXB, int NBUF>
+template <int HD, int QH, int QW, int WH, int WT, int NS, int MAXB, int NBUF, int SB>
 int launch_cfg(const RollArgs& a, const Launch& l, hipStream_t stream) {
-  auto kern = na3d_fwd_roll_kernel<HD, QH, QW, WH, WT, NS, MAXB, NBUF>;
+  auto kern = na3d_fwd_roll_kernel<HD, QH, QW, WH, WT, NS, MAXB, NBUF, SB>;
   if (l.lds_bytes > 64 * 1024 &&
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, l.lds_bytes) != hipSuccess)
@@ -509,8 +483,8 @@ int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s) {
   a.lds_rows = l.lds_rows;
   if (l.variant < 0 || l.variant >= kNumRollVariants || kRollVariants[l.variant].hd != hd) return -1;
   switch (l.variant) {
-#define NA3D_ROLL_CASE(i, HD, QH, QW, WH, WT, NS, MAXB, NBUF) \
-  case i: return launch_cfg<HD, QH, QW, WH, WT, NS, MAXB, NBUF>(a, l, s);
+#define NA3D_ROLL_CASE(i, HD, QH, QW, WH, WT, NS, MAXB, NBUF, SB) \
+  case i: return launch_cfg<HD, QH, QW, WH, WT, NS, MAXB, NBUF, SB>(a, l, s);
     NA3D_ROLL_VARIANTS(NA3D_ROLL_CASE)
 #undef NA3D_ROLL_CASE
     default: return -1;

@@ -97,7 +97,7 @@ bool plan_roll(int v, int B, int T, int H, int W, int NH, int HD, int KT, int KH
   if (un_max / 32 > rv.maxb) return false;
   const int halo_max = std::min(BH + KH - 1, H) * hwd_max;
   // K and V rows of HD*2 bytes, in one or two plane buffers
-  const int64_t lds = 2LL * rv.nbuf * halo_max * (HD * 2);
+  const int64_t lds = 2LL * rv.nbuf * (halo_max + kPadRows) * (HD * 2);
   if (lds > kMaxLdsBytes) return false;
   const int tiles_h = ceil_div(H, BH), tiles_w = ceil_div(W, rv.qw);
   const int64_t spatial = (int64_t)B * NH * tiles_h * tiles_w;
@@ -122,7 +122,7 @@ bool plan_roll(int v, int B, int T, int H, int W, int NH, int HD, int KT, int KH
   l->tiles_w = tiles_w;
   l->wgs = spatial * l->tiles_t;
   l->threads = kWave * rv.wh * rv.wt;
-  l->lds_rows = halo_max;
+  l->lds_rows = halo_max + kPadRows;
   l->lds_bytes = (int)lds;
   l->planes = std::min(T, win_start(std::min(tc, T) - 1, KT, T) + KT);
   return l->wgs <= 0x7fffffff;
@@ -133,8 +133,8 @@ bool plan_roll(int v, int B, int T, int H, int W, int NH, int HD, int KT, int KH
 int pick_roll(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, Launch* l) {
   static const int p16[] = {0};
   static const int p32[] = {1};
-  static const int p64_small[] = {2, 3, 4, 8, 6};
-  static const int p64_large[] = {8, 6, 7};
+  static const int p64_small[] = {2, 3, 4, 5, 6};
+  static const int p64_large[] = {6, 7, 8};
   static const int p128[] = {9, 10, 11};
   static const int p256[] = {12};
   const int* pref;
