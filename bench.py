@@ -7,15 +7,22 @@ A step is one na3d_fwd call over one batch of the synthetic workload (all
 inputs resident in HBM before timing starts).  The headline workload is the
 VAE-decoder tile (B=1, T=16, H=64, W=96, NH=8, HD=64, window 3x7x7).  Prints
 ONE JSON line with TFLOP/s (algorithmic FLOPs = 4*B*NH*T*H*W*KT*KH*KW*HD), the
-roofline of the kernel (HBM-bound at this arithmetic intensity: compulsory
-bytes = q, k, v read once + out written once) and the CPU oracle's throughput
-on a bounded sample of the same workload.
+roofline of the kernel (HBM-bound at this arithmetic intensity: algorithmic
+bytes = q, k, v read once + out written once = 8*HD bytes per query-head) and
+the CPU oracle's throughput on a bounded sample of the same workload.
+
+    python bench.py --copy-calibration BYTES
+
+runs a plain device-to-device copy of BYTES bytes a few times and nothing
+else: the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,6 +35,10 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 HEADLINE = "decoder_tile"
 METRIC = "NA3D fwd TFLOP/s and % bf16 MFMA peak on 1 MI355X, (3,7,7)/(11,11,11)"
+KERNEL_SOURCES = ("neighborhood_attention_amd/csrc/common.h",
+                  "neighborhood_attention_amd/csrc/kernel_roll.hip",
+                  "neighborhood_attention_amd/csrc/kernel_general.hip",
+                  "neighborhood_attention_amd/csrc/na3d.cpp")
 
 
 def parse():
@@ -41,15 +52,41 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-large-window", action="store_true",
+                    help="headline run without the 11x11x11 companion measurement")
     ap.add_argument("--no-check", action="store_true",
                     help="skip the sampled parity check before timing")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (counter calibration)")
     return ap.parse_args()
 
 
+def sources_sha256():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed counter summary of this
+    workload, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "na3d_fwd_roll_%s_traffic.md" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not sha or not tb or sha.group(1) != sources_sha256():
+        return None
+    return float(tb.group(1))
+
+
 def time_kernel(fn, steps, warmup):
-    """Warm up, then time `steps` back-to-back launches.  Returns
-    (wall ms per step, kernel ms per launch from HIP events on the launch
-    stream)."""
+    """Warm up, then time `steps` back-to-back launches.  Returns (wall ms per
+    step, kernel ms per launch from HIP events recorded on the stream the
+    kernel is launched on: torch's current stream, which fn uses)."""
     import torch
 
     for _ in range(warmup):
@@ -70,7 +107,7 @@ def time_kernel(fn, steps, warmup):
 
 def sampled_check(q, k, v, window, out, seed, npts=400):
     """Parity gate before timing (validate, then time): oracle vs GPU on
-    sampled outputs."""
+    sampled outputs.  Returns the errors and the host copies of the inputs."""
     import oracle
     import torch
 
@@ -78,11 +115,7 @@ def sampled_check(q, k, v, window, out, seed, npts=400):
     rng = np.random.default_rng(seed)
     pts = np.stack([rng.integers(0, s, npts) for s in shape[:5]], axis=1)
     idx = tuple(torch.as_tensor(pts[:, i], device=q.device) for i in range(5))
-
-    def gather_window_inputs():
-        return q.cpu(), k.cpu(), v.cpu()
-
-    qc, kc, vc = gather_window_inputs()
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
     ref = oracle.fwd_points(qc, kc, vc, window, pts)
     got = out[idx].double().cpu().numpy()
     diff = got - ref
@@ -92,7 +125,8 @@ def sampled_check(q, k, v, window, out, seed, npts=400):
 
 def cpu_baseline(host_inputs, window, seed, target_s):
     """Time the oracle (as it stands) on a bounded random sample of the
-    workload's queries; returns TFLOP/s, threads and a description."""
+    workload's query-heads, sized for about target_s seconds; returns its
+    TFLOP/s (same algorithmic FLOP count per query-head as the metric)."""
     import oracle
 
     qc, kc, vc = host_inputs
@@ -100,6 +134,7 @@ def cpu_baseline(host_inputs, window, seed, target_s):
     KT, KH, KW = window
     HD = shape[5]
     per_query = 4 * KT * KH * KW * HD
+    total_q = int(np.prod(shape[:5]))
     rng = np.random.default_rng(seed + 17)
     threads = oracle.max_threads(0)
 
@@ -109,18 +144,18 @@ def cpu_baseline(host_inputs, window, seed, target_s):
         oracle.fwd_points(qc, kc, vc, window, pts)
         return time.perf_counter() - t0
 
-    pilot_n = 2000
-    dt = run(pilot_n)
-    n = int(min(max(pilot_n * target_s / max(dt, 1e-6), pilot_n), 50_000_000))
+    pilot = min(2000, total_q)
+    dt = run(pilot)
+    n = int(min(total_q, max(pilot, pilot * target_s / max(dt, 1e-9))))
     dt = run(n)
-    total_q = int(np.prod(shape[:5]))
     return {
-        "value": n * per_query / dt / 1e12,
+        "value": round(n * per_query / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "%d random query-heads of %d (%.2f%%), %.1f s of oracle time, "
-                  "double precision, OpenMP" % (n, total_q, 100.0 * n / total_q, dt),
+        "sample": "%d random query-heads of %d (%.2f%%) of the same workload and inputs, "
+                  "%.1f s of oracle time, fp64, %d OpenMP threads"
+                  % (n, total_q, 100.0 * n / total_q, dt, threads),
     }
 
 
@@ -153,6 +188,7 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0):
     else:
         achieved, peak, unit = w.flops / kern_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     plan = na.plan(w.shape, w.window)
+    tbytes = measured_traffic(name)  # HBM bytes per launch from the counters, if current
     rec = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -171,6 +207,7 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0):
             "shape_BTHWNH_HD": list(w.shape),
             "window": list(w.window),
             "seed": w.seed,
+            "variant": plan["variant"],
             "tile": [plan["tile_t"], plan["tile_h"], plan["tile_w"]],
             "workgroups": plan["workgroups"],
         },
@@ -182,7 +219,10 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0):
             "peak": peak,
             "unit": unit,
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            # measured HBM bytes per launch over the same launch time (GB/s):
+            # comparable with `achieved` for the HBM-bound workloads
+            "traffic": None if tbytes is None else round(tbytes / kern_s / 1e9, 2),
+            "traffic_bytes_per_launch": tbytes,
         },
         "kernel_us": round(kern_ms * 1e3, 2),
         "parity_sampled": {"rel_l2": rel, "max_abs": mab},
@@ -192,17 +232,33 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0):
     return rec
 
 
+def copy_calibration(nbytes):
+    """A plain device copy of a known size, for scaling memory counters."""
+    import torch
+
+    n = max(nbytes // 2, 1)
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": 2 * n, "launches": 5}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only: the NA3D path here has no multi-GPU "
+              "code (--gpus %d requested); run with --gpus 1" % args.gpus, file=sys.stderr)
         return 2
     import torch
 
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return 0
     if args.all:
         from na3d_inputs import WORKLOADS
         for name in WORKLOADS:
@@ -212,12 +268,14 @@ def main():
         return 0
     rec = bench_workload(args.workload, args.steps, args.warmup, check=not args.no_check,
                          cpu=not args.no_cpu_baseline, cpu_s=args.cpu_seconds)
-    if args.workload == HEADLINE:
+    if args.workload == HEADLINE and not args.no_large_window:
         # the metric also names the 11x11x11 window: report it beside the headline
-        lw = bench_workload("large_window", args.steps, args.warmup, check=False, cpu=False)
+        lw = bench_workload("large_window", args.steps, args.warmup, check=not args.no_check,
+                            cpu=False)
         rec["large_window_11x11x11"] = {
             "value": lw["value"], "unit": "TFLOP/s", "mfma_peak_frac": lw["mfma_peak_frac"],
-            "ms_per_step": lw["ms_per_step"], "roofline": lw["roofline"]}
+            "ms_per_step": lw["ms_per_step"], "kernel_us": lw["kernel_us"],
+            "roofline": lw["roofline"], "parity_sampled": lw["parity_sampled"]}
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -82,11 +82,16 @@ const char* na3d_status_string(int status);
 /*
  * Launch plan na3d_fwd would use for these sizes, without touching a device:
  * plan[0] = kernel family id (1 general, 2 rolling), plan[1] = query planes
- * per workgroup, plan[2] = tile
- * extent along H, plan[3] = tile extent along W, plan[4] = workgroups,
- * plan[5] = threads per workgroup, plan[6] = dynamic LDS bytes, plan[7] = K/V
- * planes staged per workgroup.  `plan` must hold 8 ints.  Returns NA3D_OK or
- * an NA3D_ERR_* code for invalid sizes.
+ * per (middle) run of a workgroup, plan[2] = tile extent along H, plan[3] =
+ * tile extent along W, plan[4] = workgroups, plan[5] = threads per
+ * workgroup, plan[6] = dynamic LDS bytes, plan[7] = most K/V planes staged
+ * by one workgroup, plan[8] = rolling instantiation index (0 for the general
+ * family), plan[9] = workgroups along T per spatial tile (the rolling family
+ * splits T into runs of query planes, the planes that share the first or the
+ * last window in runs of their own, and a workgroup streams one or more
+ * consecutive runs).
+ * `plan` must hold 10 ints.  Returns NA3D_OK or an NA3D_ERR_* code for
+ * invalid sizes.
  */
 int na3d_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH,
               int KW, int* plan);
@@ -99,7 +104,8 @@ int na3d_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH,
  *            family (a run of query planes per workgroup)
  *   variant: rolling instantiation, 0 .. na3d_num_variants()-1 (ignored
  *            otherwise); each is compiled for one head dimension
- *   tile_t : query planes per rolling workgroup, 0 = automatic
+ *   tile_t : query planes per middle run of a rolling workgroup,
+ *            0 = automatic
  * Same pointer/layout/ownership/stream contract as na3d_fwd.  Returns
  * NA3D_ERR_CONFIG when the configuration cannot run these sizes (wrong head
  * dimension for the variant, window union or halo beyond its static limits,

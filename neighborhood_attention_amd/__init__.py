@@ -34,7 +34,7 @@ NA3D_ERR_CONFIG = -9
 EXPORTS = ("na3d_fwd", "na3d_check_args", "na3d_status_string", "na3d_plan",
            "na3d_fwd_config", "na3d_plan_config", "na3d_num_variants", "na3d_abi_version")
 PLAN_KEYS = ("family", "tile_t", "tile_h", "tile_w", "workgroups", "threads", "lds_bytes",
-             "planes")
+             "planes", "variant", "runs")
 
 _lock = threading.Lock()
 _lib = None
@@ -93,7 +93,7 @@ def plan(shape, kernel_size, family: int = 0, variant: int = 0, tile_t: int = 0)
     """Launch plan for these sizes (automatic, or an explicit configuration)."""
     B, T, H, W, NH, HD = (int(x) for x in shape)
     KT, KH, KW = (int(x) for x in kernel_size)
-    buf = (ctypes.c_int * 8)()
+    buf = (ctypes.c_int * 10)()
     rc = load().na3d_plan_config(B, T, H, W, NH, HD, KT, KH, KW, int(family), int(variant),
                                  int(tile_t), buf)
     if rc != NA3D_OK:

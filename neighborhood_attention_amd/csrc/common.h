@@ -80,6 +80,8 @@ struct Launch {
   int variant;     // index into the family's instantiation table
   int tile_t, tile_h, tile_w;
   int tiles_t, tiles_h, tiles_w;
+  int ta, tz;      // rolling: first run [0, ta), last run [tz, T) (ta = 0 / tz = T: none)
+  int nruns, rpw;  // rolling: runs along T, consecutive runs per workgroup
   int64_t wgs;
   int threads;
   int lds_rows;    // rows of each K and V staging buffer
@@ -88,35 +90,48 @@ struct Launch {
 };
 
 // Instantiations of the rolling family: index, head dim, query block
-// (QH x QW = 16), wave grid (WH block rows x WT query-plane phases), query-plane
-// slots per wave, the most full 32-key blocks a wave's window union may hold,
-// the number of staged plane buffers, and the blocks per softmax group.
-#define NA3D_ROLL_VARIANTS(X)             \
-  X(0, 16, 2, 8, 1, 4, 1, 4, 2, 5)        \
-  X(1, 32, 2, 8, 1, 4, 1, 4, 2, 5)        \
-  X(2, 64, 2, 8, 1, 4, 1, 4, 2, 5)        \
-  X(3, 64, 2, 8, 2, 4, 1, 4, 1, 5)        \
-  X(4, 64, 2, 8, 1, 4, 1, 4, 1, 5)        \
-  X(5, 64, 2, 8, 2, 2, 2, 4, 2, 5)        \
-  X(6, 64, 4, 4, 1, 8, 2, 7, 1, 4)        \
-  X(7, 64, 4, 4, 1, 8, 2, 7, 1, 2)        \
-  X(8, 64, 4, 4, 1, 4, 4, 7, 1, 2)        \
-  X(9, 128, 2, 8, 1, 4, 1, 4, 1, 5)       \
-  X(10, 128, 2, 8, 1, 4, 1, 4, 2, 5)      \
-  X(11, 128, 2, 8, 2, 2, 2, 4, 1, 5)      \
-  X(12, 256, 2, 8, 1, 4, 1, 4, 1, 5)
-
-// Zeroed rows past the staged halo in each rolling plane buffer: the union's
-// partial last block reads at most 15 rows past the halo.
-constexpr int kPadRows = 16;
+// (QH x QW = 16 queries per wave), wave grid (WH block rows x WT query-plane
+// phases), query-plane slots per wave, 16-key tiles per softmax group, most
+// groups a wave's window union may need, and staged plane buffers (1 or 2).
+#define NA3D_ROLL_VARIANTS(X)               \
+  X(0, 64, 2, 8, 1, 3, 1, 7, 1, 2)          \
+  X(1, 64, 2, 8, 2, 3, 1, 7, 1, 2)          \
+  X(2, 64, 4, 4, 2, 3, 1, 7, 1, 2)          \
+  X(3, 64, 2, 8, 4, 3, 1, 7, 1, 1)          \
+  X(4, 64, 2, 8, 2, 3, 1, 7, 1, 1)          \
+  X(5, 64, 4, 4, 1, 4, 1, 13, 1, 1)         \
+  X(6, 64, 4, 4, 1, 8, 1, 13, 1, 1)         \
+  X(7, 64, 4, 4, 2, 4, 1, 13, 1, 1)         \
+  X(8, 64, 2, 8, 1, 3, 1, 4, 1, 2)          \
+  X(9, 64, 2, 8, 1, 3, 1, 7, 2, 2)          \
+  X(10, 64, 4, 4, 1, 4, 1, 13, 2, 1)        \
+  X(11, 16, 2, 8, 1, 3, 1, 7, 2, 2)         \
+  X(12, 32, 2, 8, 1, 3, 1, 7, 2, 2)         \
+  X(13, 128, 2, 8, 1, 3, 1, 7, 1, 2)        \
+  X(14, 128, 2, 8, 2, 3, 1, 7, 1, 1)        \
+  X(15, 128, 2, 8, 1, 3, 1, 7, 2, 1)        \
+  X(16, 128, 4, 4, 1, 4, 1, 13, 1, 1)       \
+  X(17, 256, 2, 8, 1, 3, 1, 7, 2, 1)        \
+  X(18, 64, 2, 8, 4, 3, 1, 7, 1, 2)         \
+  X(19, 64, 4, 4, 4, 3, 1, 7, 1, 2)         \
+  X(20, 64, 2, 8, 1, 4, 1, 7, 1, 2)         \
+  X(21, 64, 2, 8, 1, 4, 1, 7, 1, 1)         \
+  X(22, 64, 4, 4, 1, 4, 1, 7, 2, 1)         \
+  X(23, 64, 4, 4, 1, 4, 1, 7, 2, 2)         \
+  X(24, 64, 4, 4, 2, 4, 1, 7, 2, 1)         \
+  X(25, 128, 2, 8, 1, 4, 1, 7, 1, 1)        \
+  X(26, 64, 2, 8, 2, 2, 2, 7, 1, 2)         \
+  X(27, 64, 2, 8, 4, 1, 3, 4, 2, 1)         \
+  X(28, 64, 2, 8, 2, 1, 3, 4, 2, 2)         \
+  X(29, 128, 2, 8, 2, 2, 2, 4, 2, 1)
 
 struct RollVariant {
-  int hd, qh, qw, wh, wt, ns, maxb, nbuf, sb;
+  int hd, qh, qw, wh, wt, ns, nk, ng, nbuf;
 };
 
 constexpr RollVariant kRollVariants[] = {
-#define NA3D_ROLL_ENTRY(i, HD, QH, QW, WH, WT, NS, MAXB, NBUF, SB) \
-  {HD, QH, QW, WH, WT, NS, MAXB, NBUF, SB},
+#define NA3D_ROLL_ENTRY(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF) \
+  {HD, QH, QW, WH, WT, NS, NK, NG, NBUF},
     NA3D_ROLL_VARIANTS(NA3D_ROLL_ENTRY)
 #undef NA3D_ROLL_ENTRY
 };

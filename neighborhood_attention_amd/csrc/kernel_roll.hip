@@ -10,44 +10,57 @@
 // (ih, it) owns the QH x QW block of 16 queries in block row ih, for the query
 // planes t0 + it, t0 + it + WT, ... of the run.  All waves share the same
 // query columns, so the union of a block's windows is one contiguous range of
-// the staged halo rows: key u of the union sits in LDS row base + u, and
-// every K/V operand address is a lane constant plus a block offset.
+// the staged halo rows, and every K/V operand address is a lane constant plus
+// a compile-time tile offset.
 //
-// The WG streams the key planes of the run in order.  Each plane's K/V halo
+// The WG streams the key planes of its run in order.  Each plane's K/V halo
 // is staged in LDS once, with direct global->LDS loads (global_load_lds
 // dwordx4), into one or two plane buffers (with two, plane t'+1 is in flight
 // while plane t' is computed).  Staged rows are unpadded and XOR-swizzled in
 // 16-byte chunks (see swz), which keeps both operand reads free of bank
 // conflicts.  A wave keeps the online-softmax state of up to NS of its query
-// planes (a ring: a query plane is admitted when the stream reaches its
-// window start and retired, output written, after its last key plane), and
-// reuses every K/V fragment it reads from LDS for all of them.
+// planes (admitted when the stream reaches their window start, retired after
+// their last key plane) and reuses every K/V fragment it reads for all of them.
 //
-// Within a 16-key tile the keys feed the MFMA rows in the order key_perm
-// (chosen for conflict-free LDS reads); K rows, V rows and window masks all
-// use that order.
+// Runs: the first query planes of an axis share the window [0, KT), and so do
+// the last ones.  The host may give those planes runs of their own, so that
+// in the middle runs a wave's consecutive query planes (WT apart) have
+// disjoint windows and WT = KT keeps every wave busy on every key plane.
 //
-// Per key plane, a wave walks its union in groups of up to SB 32-key blocks;
-// each group runs three phases, each over all of its blocks and all active
-// query planes, so the MFMAs and exponentials of a phase are independent:
+// Per key plane a wave reads a window of 16*NK*ngrp staged rows that covers
+// its union (shifted down where it would pass the end of the buffer), in
+// ngrp groups of NK 16-key tiles.  Each group runs three phases, each over
+// all of its tiles and all active query planes, with no data-dependent
+// branches inside, so the MFMAs and exponentials of a phase are independent:
 //   S^T = K . Q^T + bias    bf16 MFMA 16x16x32; bias (0 or -inf) is the
 //                           window mask, computed once per wave and fed in
 //                           as the accumulator input, so masking costs no VALU
 //   softmax                 one exact max over the group's scores, one
 //                           rescale of the running output, then exp2
-//   O^T += V^T . P^T        bf16 MFMA; the S^T accumulator layout is already
-//                           the P^T operand, V^T comes from the transpose read
-// The union's last partial block uses a 16-key step (MFMA 16x16x16) when it
-// holds at most 16 keys.  Its masked keys read staged rows past the union;
-// each plane buffer carries kPadRows zeroed rows past the halo, so such rows
-// always hold finite values (which the -inf bias then removes).
+//   O^T += V^T . P^T        bf16 MFMA 16x16x32 per pair of tiles (16x16x16
+//                           for an odd last tile); the S^T accumulator layout
+//                           is already the P^T operand, V^T comes from the
+//                           transpose read
+// Rows past the staged halo are zeroed once, so every row read holds finite
+// values and masked keys contribute exactly zero.
+//
+// Global memory traffic is arranged so that compute never waits on it:
+// a query plane's Q is fetched one key plane ahead into spare registers, and
+// a retired plane's output is packed into registers and stored after the
+// next barrier, so the one wait per key plane (for the staged plane) does
+// not also wait for fresh stores.
 #include "common.h"
 
 namespace na3d {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
+// Natural-log headroom before the reference max is moved: unnormalised
+// weights stay below e^8 (about 3000), far inside bf16 and fp32 range.
+constexpr float kRescale = 8.f;
 constexpr uint32_t kBf16NegInf = 0xff80u;
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left free (gfx9 layout)
+constexpr int kWaitVm0 = 0x0f70;
 
 struct RollArgs {
   const uint16_t* q;
@@ -57,9 +70,36 @@ struct RollArgs {
   int B, T, H, W, NH;
   int KT, KH, KW;
   int tiles_t, tiles_h, tiles_w;
-  int tc;        // query planes per workgroup
+  int tc;        // query planes per middle run
+  int ta;        // first run [0, ta); 0 = none
+  int tz;        // last run [tz, T); T = none
+  int nruns;     // runs along T
+  int rpw;       // consecutive runs streamed by one workgroup
   int lds_rows;  // rows of each K and V staging buffer
 };
+
+// Max over the 4 lanes (l, l^16, l^32, l^48) that hold one query,
+// with the gfx950 row-swap permutes (VALU only, no LDS round trip).  After
+// v_permlane16_swap a, b (both holding x), a and b hold x of lanes l and
+// l^16 in some order; v_permlane32_swap does the same for l^32.  Written as
+// inline assembly: the compiler folds the builtin's two results into one
+// when both inputs are the same value.  The s_nop covers the VALU-write ->
+// permlane-read hazard.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float xmax4(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  x = fmaxf(a, b);
+  a = x;
+  b = x;
+  swap32(a, b);
+  return fmaxf(a, b);
+}
 
 template <int HD>
 struct Slot {
@@ -67,16 +107,16 @@ struct Slot {
   static constexpr int MT = HD / 16;
   bf16x8 qf[KSTEPS];  // Q^T operand: lane (q16, g) holds head dims [32ks + 8g, +8)
   f32x4 acc[MT];      // O^T: lane (q16, g) holds head dims 16mt + 4g + r
-  float m;            // running max (natural units), -inf before any key
-  float l;            // this lane's share of the softmax denominator
+  f32x4 accl;         // softmax denominator: the same P^T against a V^T row of ones
+  float m;            // reference max (natural units), -inf before any key
 };
 
 template <int HD>
-__device__ __forceinline__ void load_q(Slot<HD>& S, const uint16_t* qp, int g) {
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[Slot<HD>::KSTEPS], const uint16_t* qp, int g) {
 #pragma unroll
   for (int ks = 0; ks < Slot<HD>::KSTEPS; ++ks) {
     const int d = 32 * ks + 8 * g;
-    S.qf[ks] = d < HD ? *reinterpret_cast<const bf16x8*>(qp + d) : bf16x8{};
+    qf[ks] = d < HD ? *reinterpret_cast<const bf16x8*>(qp + d) : bf16x8{};
   }
 }
 
@@ -84,25 +124,29 @@ template <int HD>
 __device__ __forceinline__ void reset_state(Slot<HD>& S) {
 #pragma unroll
   for (int mt = 0; mt < Slot<HD>::MT; ++mt) S.acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  S.accl = f32x4{0.f, 0.f, 0.f, 0.f};
   S.m = kNegInf;
-  S.l = 0.f;
 }
 
+// Normalised output of a retired query plane, packed as bf16 (RNE) for the
+// 8-byte stores of lane (q16, g): head dims 16mt + 4g .. +3.
 template <int HD>
-__device__ __forceinline__ void slot_finish(Slot<HD>& S, uint16_t* op, int g, bool qvalid) {
-  float l = S.l;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (qvalid) {
-    const float inv = 1.f / l;
+__device__ __forceinline__ void pack_out(const Slot<HD>& S, uint32_t (&pk)[2 * Slot<HD>::MT]) {
+  const float inv = 1.f / S.accl[0];
 #pragma unroll
-    for (int mt = 0; mt < Slot<HD>::MT; ++mt) {
-      const bf16x2 lo = {(__bf16)(S.acc[mt][0] * inv), (__bf16)(S.acc[mt][1] * inv)};
-      const bf16x2 hi = {(__bf16)(S.acc[mt][2] * inv), (__bf16)(S.acc[mt][3] * inv)};
-      *reinterpret_cast<uint2*>(op + 16 * mt + 4 * g) =
-          make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-    }
+  for (int mt = 0; mt < Slot<HD>::MT; ++mt) {
+    const bf16x2 lo = {(__bf16)(S.acc[mt][0] * inv), (__bf16)(S.acc[mt][1] * inv)};
+    const bf16x2 hi = {(__bf16)(S.acc[mt][2] * inv), (__bf16)(S.acc[mt][3] * inv)};
+    pk[2 * mt] = __builtin_bit_cast(uint32_t, lo);
+    pk[2 * mt + 1] = __builtin_bit_cast(uint32_t, hi);
   }
+}
+
+template <int MT>
+__device__ __forceinline__ void store_out(uint16_t* op, const uint32_t (&pk)[2 * MT], int g) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    *reinterpret_cast<uint2*>(op + 16 * mt + 4 * g) = make_uint2(pk[2 * mt], pk[2 * mt + 1]);
 }
 
 // V^T operand through the transpose read: lane (4j + a) of a 16-lane group
@@ -129,18 +173,42 @@ __device__ __forceinline__ int v_addr(int r, int mt, int q16) {
   return r * (HD * 2) + (((2 * mt + ((q16 & 3) >> 1)) ^ swz(HD, r)) << 4) + ((q16 & 1) << 3);
 }
 
-// Window-mask bias of 8 scores packed as bf16 pairs (0 or -inf), expanded to
-// the two f32x4 accumulator inputs of a 32-key block.
-__device__ __forceinline__ void unpack_bias(const uint32_t (&w)[4], f32x4& b0, f32x4& b1) {
-  b0 = f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
-             __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xffff0000u)};
-  b1 = f32x4{__builtin_bit_cast(float, w[2] << 16), __builtin_bit_cast(float, w[2] & 0xffff0000u),
-             __builtin_bit_cast(float, w[3] << 16), __builtin_bit_cast(float, w[3] & 0xffff0000u)};
+// Direct global->LDS load of 16 bytes per lane: lane L's bytes land at LDS
+// address lds + 16 L.  Written as inline assembly so that the compiler does
+// not see an LDS write in flight: it would otherwise wait for it (vmcnt(0))
+// before every transpose read, stalling compute on the next plane's
+// staging.  The kernel waits for these loads itself, before the barrier that
+// hands a staged plane to compute.  M0 (the LDS base operand) is restored;
+// the s_nop keeps the wait state the hardware needs between an M0 write and
+// an LDS DMA (the compiler inserts the same one for its own sequence).
+// The source address is a wave-uniform base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16(const void* base, uint32_t ofs, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(ofs), "s"(base), "s"(lds)
+      : "memory");
 }
 
-template <int HD, int QH, int QW, int WH, int WT, int NS, int MAXB, int NBUF, int SB>
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+
+// Window-mask bias of the 4 scores of a 16-key tile, packed as bf16 pairs
+// (0 or -inf), expanded to the f32x4 accumulator input.
+__device__ __forceinline__ f32x4 unpack_bias(const uint32_t (&w)[2]) {
+  return f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
+               __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xffff0000u)};
+}
+
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF>
 __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const RollArgs a) {
-  constexpr int NGRP = (MAXB + 1 + SB - 1) / SB;  // groups covering MAXB full blocks + a tail
   static_assert(QH * QW == 16, "a wave owns 16 queries");
   static_assert(NBUF == 1 || NBUF == 2, "one or two plane buffers");
   constexpr int KSTEPS = Slot<HD>::KSTEPS;
@@ -150,6 +218,14 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
   constexpr int BH = WH * QH;
   constexpr int NT = kWave * WH * WT;
   constexpr int RSTEP = NT / CPR;  // staged rows per DMA round
+  constexpr int GK = 16 * NK;      // keys per softmax group
+  constexpr int NP = NK / 2;       // 32-key tile pairs per group
+  constexpr bool ODD = (NK & 1) != 0;
+  // V^T operands of all ones (bf16 1.0): the MFMA against P^T sums the
+  // weights of each query, already reduced over its four lanes
+  const bf16x8 kOnes8 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  const s16x4 kOnes4 = {0x3f80, 0x3f80, 0x3f80, 0x3f80};
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int buf_bytes = a.lds_rows * RB;  // one K or V plane buffer
@@ -165,7 +241,7 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
   const int ih = wave % WH;
   const int it = wave / WH;
 
-  // ---- workgroup -> (b, n, tile_h, tile_w, tile_t); tile_t varies fastest
+  // ---- workgroup -> (b, n, tile_h, tile_w, run group); run groups vary fastest
   int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int tt = wg % a.tiles_t;
   wg /= a.tiles_t;
@@ -177,7 +253,21 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
   const int b = wg / a.NH;
 
   const int T = a.T, H = a.H, W = a.W, KT = a.KT, KH = a.KH, KW = a.KW;
-  const int t0 = tt * a.tc, t1 = min(t0 + a.tc, T);
+  // query planes [t0, t1) of run ri
+  auto run_bounds = [&](int ri, int& t0, int& t1) {
+    const int mid = ri - (a.ta > 0 ? 1 : 0);
+    if (a.ta > 0 && ri == 0) {
+      t0 = 0;
+      t1 = a.ta;
+    } else if (a.tz < T && ri == a.nruns - 1) {
+      t0 = a.tz;
+      t1 = T;
+    } else {
+      t0 = a.ta + mid * a.tc;
+      t1 = min(t0 + a.tc, a.tz);
+    }
+  };
+  const int r_lo = tt * a.rpw, r_hi = min(r_lo + a.rpw, a.nruns);
   const int h0 = th * BH, w0 = tw * QW;
   const int h1 = min(h0 + BH, H) - 1, w1 = min(w0 + QW, W) - 1;
   // halo of the tile: rows [hh0, hh0 + hhn) x columns [hw0, hw0 + hwd)
@@ -190,7 +280,7 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
 
   // ---- this wave's block of 16 queries
   const int bh0 = h0 + ih * QH;
-  const bool active = bh0 < H && t0 + it < t1;
+  const bool active = bh0 < H;
   const int bh1 = min(bh0 + QH, H) - 1;
   const int qh = bh0 + q16 / QW;
   const int qw = w0 + q16 % QW;
@@ -198,38 +288,40 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
   const int qhc = min(qh, H - 1), qwc = min(qw, W - 1);
   const int ash = win_start(qhc, KH, H);
   const int asw = win_start(qwc, KW, W);
-  // union of the block's windows = staged rows [base, base + un)
+  // union of the block's windows = staged rows [base, base + un); the wave
+  // reads rows [rb, rb + ngrp * GK), which hold the union and stay in the buffer
   const int uh0 = bh0 < H ? win_start(bh0, KH, H) : hh0;
   const int un = active ? (win_start(bh1, KH, H) + KH - uh0) * hwd : 0;
   const int base = (uh0 - hh0) * hwd;
-  const int nblk = (un + 31) >> 5;  // 32-key blocks, the last possibly partial
+  const int ngrp = (un + GK - 1) / GK;
+  const int rb = max(0, min(base, a.lds_rows - ngrp * GK));
 
-  // ---- window masks, packed as bf16 pairs (0 = in window, -inf = out)
+  // ---- window masks of every tile, packed as bf16 pairs (0 = in window)
   const float inv_hwd = 1.f / (float)hwd;
-  auto key_out = [&](int u) -> uint32_t {
-    if (!qvalid || u >= un) return kBf16NegInf;
-    int uh = (int)((float)u * inv_hwd);
-    int uw = u - uh * hwd;
+  auto key_out = [&](int r) -> uint32_t {
+    if (!qvalid || r >= halo_rows) return kBf16NegInf;
+    int uh = (int)((float)r * inv_hwd);
+    int uw = r - uh * hwd;
     if (uw < 0) { --uh; uw += hwd; }
     if (uw >= hwd) { ++uh; uw -= hwd; }
-    const bool in = (unsigned)(uh0 + uh - ash) < (unsigned)KH &&
+    const bool in = (unsigned)(hh0 + uh - ash) < (unsigned)KH &&
                     (unsigned)(hw0 + uw - asw) < (unsigned)KW;
     return in ? 0u : kBf16NegInf;
   };
-  auto bias_words = [&](int u0, uint32_t (&w)[4]) {
+  uint32_t bias[NG][NK][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // score slot r of tile ct holds key 16ct + key_perm(4g + r)
-      const int r = 2 * (i & 1);
-      const int u = u0 + 16 * (i >> 1);
-      w[i] = key_out(u + key_perm(HD, 4 * g + r)) | (key_out(u + key_perm(HD, 4 * g + r + 1)) << 16);
-    }
-  };
-  uint32_t bias[MAXB + 1][4];  // MAXB full blocks and the tail
+  for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-  for (int bb = 0; bb <= MAXB; ++bb) bias_words(32 * bb, bias[bb]);
+    for (int c = 0; c < NK; ++c)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        // score slot r of a tile holds key key_perm(4g + r) of the tile
+        const int r0 = rb + GK * gi + 16 * c;
+        bias[gi][c][i] = key_out(r0 + key_perm(HD, 4 * g + 2 * i)) |
+                         (key_out(r0 + key_perm(HD, 4 * g + 2 * i + 1)) << 16);
+      }
 
-  // ---- operand offsets inside one plane buffer; blocks add multiples of 16
+  // ---- operand offsets inside one plane buffer; tiles add multiples of 16
   // rows, which leave the swizzle unchanged
   // K operand: lane (q16, g) holds key kp of a tile; V operand (transpose
   // read): lane (4j + a) of group g addresses key vp = key_perm(4g + j)
@@ -237,9 +329,9 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
   const int vp = key_perm(HD, 4 * g + (q16 >> 2));
   int kofs[KSTEPS], vofs[MT];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) kofs[ks] = k_addr<HD>(base + kp, 4 * ks + g);
+  for (int ks = 0; ks < KSTEPS; ++ks) kofs[ks] = k_addr<HD>(rb + kp, 4 * ks + g);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) vofs[mt] = v_addr<HD>(base + vp, mt, q16);
+  for (int mt = 0; mt < MT; ++mt) vofs[mt] = v_addr<HD>(rb + vp, mt, q16);
 
   const int64_t tok = (int64_t)a.NH * HD;
   const int64_t plane = (int64_t)H * W * tok;
@@ -247,37 +339,41 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
   const int64_t qtok = ((int64_t)qhc * W + qwc) * tok;
 
   // ---- DMA staging walk: round k moves chunks [k*NT, (k+1)*NT); lane P of a
-  // wave lands at chunk P of the buffer (row P / CPR, physical chunk P % CPR)
+  // wave lands at chunk P of the buffer (row P / CPR, physical chunk P % CPR).
+  // A thread's source offsets (bytes within a plane) advance by RSTEP halo
+  // rows per round; they are the same for every plane.
   const int pc = tid % CPR;
   const int row0 = tid / CPR;
   const int step_h = RSTEP / hwd, step_w = RSTEP % hwd;
-  const int row0_h = row0 / hwd, row0_w = row0 % hwd;
+  const uint32_t tok_b = (uint32_t)(a.NH * HD * 2);               // bytes per token
+  const uint32_t dstep = (uint32_t)(step_h * W + step_w) * tok_b;  // one round
+  const uint32_t dwrap = (uint32_t)(W - hwd) * tok_b;              // halo row carry
+  const int rw0 = row0 % hwd;
+  const uint32_t d0 = (uint32_t)((hh0 + row0 / hwd) * W + hw0 + rw0) * tok_b + (uint32_t)(n * HD * 2);
   auto issue_stage = [&](int tp, int bufi) {
-    const uint16_t* kp = a.k + bbase + (int64_t)tp * plane;
-    const uint16_t* vp = a.v + bbase + (int64_t)tp * plane;
-    unsigned char* dk = smem + bufi * 2 * buf_bytes + wave * kWave * 16;
-    unsigned char* dv = dk + buf_bytes;
-    int rh = row0_h, rw = row0_w;
+    const uint16_t* kpl = a.k + (int64_t)b * T * plane + (int64_t)tp * plane;
+    const uint16_t* vpl = a.v + (int64_t)b * T * plane + (int64_t)tp * plane;
+    const uint32_t dk = lds_addr(smem + bufi * 2 * buf_bytes + wave * kWave * 16);
+    const uint32_t dv = dk + buf_bytes;
+    uint32_t d = d0;
+    int rw = rw0;
     for (int c0 = 0, row = row0; c0 < total_chunks; c0 += NT, row += RSTEP) {
       if (c0 + tid < total_chunks) {
-        const int64_t off = ((int64_t)(hh0 + rh) * W + (hw0 + rw)) * tok + ((pc ^ swz(HD, row)) << 3);
-        __builtin_amdgcn_global_load_lds(kp + off, (__attribute__((address_space(3))) void*)(dk + c0 * 16), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vp + off, (__attribute__((address_space(3))) void*)(dv + c0 * 16), 16, 0, 0);
+        const uint32_t o = d + (uint32_t)((pc ^ swz(HD, row)) << 4);
+        dma16(kpl, o, dk + c0 * 16);
+        dma16(vpl, o, dv + c0 * 16);
       }
-      rh += step_h;
+      d += dstep;
       rw += step_w;
-      if (rw >= hwd) { rw -= hwd; ++rh; }
+      if (rw >= hwd) {
+        rw -= hwd;
+        d += dwrap;
+      }
     }
   };
 
-  // this wave's query planes: t0 + it + WT * j, j = 0, 1, ...; slot j % NS
-  auto tq = [&](int j) { return t0 + it + WT * j; };
-  Slot<HD> S[NS];
-  unsigned preloaded = 0;  // slots whose Q was fetched one plane early
-  int jlo = 0, jhi = -1;   // query planes j in [jlo, jhi] are in flight
-  const int p0 = win_start(t0, KT, T), p1 = win_start(t1 - 1, KT, T) + KT;
-  // zero the rows past the halo in every buffer (never staged; read only by
-  // masked tail keys); the first barrier of the stream orders these stores
+  // zero the rows past the halo in every buffer (never staged; read only as
+  // masked keys); the first barrier of the stream orders these stores
   {
     const int pad16 = (a.lds_rows - halo_rows) * (RB / 16);
     for (int i = tid; i < 2 * NBUF * pad16; i += NT) {
@@ -286,181 +382,212 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
           make_uint4(0, 0, 0, 0);
     }
   }
-  issue_stage(p0, NBUF == 2 ? (p0 & 1) : 0);  // key plane tp lives in buffer tp % NBUF
-  for (int tp = p0; tp < p1; ++tp) {
-    // admit this wave's query planes whose window starts here
-    while (tq(jhi + 1) < t1 && win_start(tq(jhi + 1), KT, T) <= tp) {
-      ++jhi;
-      const int sl = jhi % NS;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        if (s == sl) {
-          if (!((preloaded >> s) & 1)) load_q(S[s], a.q + bbase + (int64_t)tq(jhi) * plane + qtok, g);
-          reset_state(S[s]);
-        }
-      preloaded &= ~(1u << sl);
-    }
-    // plane tp has landed (own DMA + Q loads); with two buffers every wave is
-    // also done with plane tp - 1, whose buffer is refilled next
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (NBUF == 2 && tp + 1 < p1) issue_stage(tp + 1, (tp + 1) & 1);
-    // fetch Q of query planes that start at the next key plane, where their
-    // slot is already free, so the load hides behind this plane's work
-    for (int j = jhi + 1; tq(j) < t1 && win_start(tq(j), KT, T) == tp + 1; ++j) {
-      if (j - NS >= jlo) break;
-      const int sl = j % NS;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        if (s == sl) load_q(S[s], a.q + bbase + (int64_t)tq(j) * plane + qtok, g);
-      preloaded |= 1u << sl;
-    }
 
-    if (active && jhi >= jlo) {
-      const unsigned char* lk = smem + (NBUF == 2 ? (tp & 1) : 0) * 2 * buf_bytes;
-      const unsigned char* lv = lk + buf_bytes;
-      bool sact[NS];
+  // the workgroup streams the key planes of runs [r_lo, r_hi) one after the
+  // other; within a run, this wave's query planes are t0 + it + WT * j,
+  // j = 0, 1, ..., held in slot j % NS
+  Slot<HD> S[NS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) sact[s] = ((s - jlo % NS + NS) % NS) < (jhi - jlo + 1);
-      // The union is processed in groups of SB 32-key blocks; each group runs
-      // three phases over all of its blocks and all active query planes:
-      // scores, softmax (one exact group max, one rescale), P.V.
+  for (int s = 0; s < NS; ++s) {
 #pragma unroll
-      for (int grp = 0; grp < NGRP; ++grp) {
-        if (grp * SB >= nblk) break;
-        f32x4 sc[NS][SB][2];
-        // ---- phase 1: S^T = K . Q^T + mask for every block of the group
+    for (int ks = 0; ks < KSTEPS; ++ks) S[s].qf[ks] = bf16x8{};
+    reset_state(S[s]);
+  }
+  bf16x8 qn[KSTEPS];          // Q of query plane qn_t, fetched one key plane early
+  int qn_t = -1;
+  uint32_t pend[2 * MT];      // packed output of a retired query plane ...
+  uint16_t* pend_p = a.o;     // ... and where it goes
+  bool pend_on = false;
+  int t0, t1;
+  run_bounds(r_lo, t0, t1);
+  issue_stage(win_start(t0, KT, T), 0);  // step st uses buffer st % NBUF
+  int st = 0;
+  for (int ri = r_lo; ri < r_hi; ++ri) {
+    if (ri > r_lo) run_bounds(ri, t0, t1);
+    const int p0 = win_start(t0, KT, T), p1 = win_start(t1 - 1, KT, T) + KT;
+    int nt0 = 0, nt1 = 0, np0 = -1;  // the next run, whose first plane follows p1 - 1
+    if (ri + 1 < r_hi) {
+      run_bounds(ri + 1, nt0, nt1);
+      np0 = win_start(nt0, KT, T);
+    }
+    auto tq = [&](int j) { return t0 + it + WT * j; };
+    int jlo = 0, jhi = -1;  // query planes j in [jlo, jhi] are in flight
+    for (int tp = p0; tp < p1; ++tp, ++st) {
+      // admit this wave's query planes whose window starts here
+      while (tq(jhi + 1) < t1 && win_start(tq(jhi + 1), KT, T) <= tp) {
+        ++jhi;
+        const int sl = jhi % NS;
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
-          const int bi = grp * SB + j;
-          if (bi > MAXB || bi >= nblk) break;
-          const bool half = 32 * bi + 16 >= un;  // a tail of at most 16 keys
-          bf16x8 kf[2][KSTEPS];
+        for (int s = 0; s < NS; ++s)
+          if (s == sl) {
+            if (qn_t == tq(jhi)) {
 #pragma unroll
-          for (int ks = 0; ks < KSTEPS; ++ks) {
-            const bool use = 32 * ks + 8 * g < HD;
-            const unsigned char* ka = lk + kofs[ks] + 32 * bi * RB;
-            kf[0][ks] = use ? *reinterpret_cast<const bf16x8*>(ka) : bf16x8{};
-            kf[1][ks] = bf16x8{};
-            if (!half) kf[1][ks] = use ? *reinterpret_cast<const bf16x8*>(ka + 16 * RB) : bf16x8{};
-          }
-          f32x4 b0, b1;
-          unpack_bias(bias[bi], b0, b1);
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            sc[s][j][0] = b0;
-            sc[s][j][1] = b1;
-            if (!sact[s]) continue;
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-              sc[s][j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][ks], S[s].qf[ks], sc[s][j][0], 0, 0, 0);
-              if (!half)
-                sc[s][j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][ks], S[s].qf[ks], sc[s][j][1], 0, 0, 0);
+              for (int ks = 0; ks < KSTEPS; ++ks) S[s].qf[ks] = qn[ks];
+            } else {
+              load_q<HD>(S[s].qf, a.q + bbase + (int64_t)tq(jhi) * plane + qtok, g);
             }
+            reset_state(S[s]);
           }
+      }
+      // plane tp has landed (with every earlier load and store of this wave);
+      // with two buffers every wave is also done with the previous step,
+      // whose buffer is refilled next
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      if (pend_on) {
+        if (qvalid) store_out<MT>(pend_p, pend, g);
+        pend_on = false;
+      }
+      const int nxt = tp + 1 < p1 ? tp + 1 : np0;  // plane of the next step, -1 = none
+      if (NBUF == 2 && nxt >= 0) issue_stage(nxt, (st + 1) & 1);
+      // fetch Q of the query plane (if any) this wave admits at the next step
+      {
+        int tn = -1;
+        if (tp + 1 < p1) {
+          if (tq(jhi + 1) < t1 && win_start(tq(jhi + 1), KT, T) == tp + 1) tn = tq(jhi + 1);
+        } else if (np0 >= 0 && nt0 + it < nt1 && win_start(nt0 + it, KT, T) == np0) {
+          tn = nt0 + it;
         }
-        // ---- phase 2: softmax over the group (the masked half of a 16-key
-        // tail block holds -inf and contributes nothing)
-        bf16x8 pf[NS][SB];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          if (!sact[s]) continue;
-          float mx = kNegInf;
-#pragma unroll
-          for (int j = 0; j < SB; ++j) {
-            const int bi = grp * SB + j;
-            if (bi > MAXB || bi >= nblk) break;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fmaxf(sc[s][j][0][r], sc[s][j][1][r]));
-          }
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float mn = fmaxf(S[s].m, mx);
-          const float alpha = S[s].m == kNegInf ? 0.f : __builtin_amdgcn_exp2f((S[s].m - mn) * kLog2e);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) S[s].acc[mt] *= alpha;
-          S[s].m = mn;
-          const float mb = mn == kNegInf ? 0.f : mn * kLog2e;
-          float sum0 = 0.f, sum1 = 0.f;
-#pragma unroll
-          for (int j = 0; j < SB; ++j) {
-            const int bi = grp * SB + j;
-            if (bi > MAXB || bi >= nblk) break;
-            float p[8];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s][j][0][r], kLog2e, -mb));
-              p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s][j][1][r], kLog2e, -mb));
-            }
-            sum0 += (p[0] + p[1]) + (p[2] + p[3]);
-            sum1 += (p[4] + p[5]) + (p[6] + p[7]);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) pf[s][j][r] = (__bf16)p[r];
-          }
-          S[s].l = S[s].l * alpha + (sum0 + sum1);
+        if (tn >= 0) {
+          load_q<HD>(qn, a.q + bbase + (int64_t)tn * plane + qtok, g);
+          qn_t = tn;
         }
-        // ---- phase 3: O^T += V^T . P^T for every block of the group
+      }
+
+      if (active && jhi >= jlo) {
+        const unsigned char* lk = smem + (NBUF == 2 ? (st & 1) : 0) * 2 * buf_bytes;
+        const unsigned char* lv = lk + buf_bytes;
+        bool sact[NS];
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
-          const int bi = grp * SB + j;
-          if (bi > MAXB || bi >= nblk) break;
-          const bool half = 32 * bi + 16 >= un;
-          if (half) {
-            s16x4 vf[MT];
+        for (int s = 0; s < NS; ++s) sact[s] = ((s - jlo % NS + NS) % NS) < (jhi - jlo + 1);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) vf[mt] = load_vt(lv, vofs[mt] + 32 * bi * RB);
+        for (int gi = 0; gi < NG; ++gi) {
+          if (gi >= ngrp) break;
+          const int gofs = GK * gi * RB;
+          // The MFMAs of phases 1 and 3 also run for free slots (on zero
+          // weights and stale Q; admission resets the slot), so that these
+          // phases hold no branches and their operand reads issue early.
+          // ---- phase 1: S^T = K . Q^T + mask, every tile of the group
+          f32x4 sc[NS][NK];
+#pragma unroll
+          for (int c = 0; c < NK; ++c) {
+            bf16x8 kf[KSTEPS];
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+              kf[ks] = (32 * ks + 8 * g < HD)
+                           ? *reinterpret_cast<const bf16x8*>(lk + kofs[ks] + gofs + 16 * c * RB)
+                           : bf16x8{};
+            const f32x4 bc = unpack_bias(bias[gi][c]);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-              if (!sact[s]) continue;
-              const bf16x4 lo = {pf[s][j][0], pf[s][j][1], pf[s][j][2], pf[s][j][3]};
-              const s16x4 pb = __builtin_bit_cast(s16x4, lo);
+              sc[s][c] = bc;
 #pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-                S[s].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[mt], pb, S[s].acc[mt], 0, 0, 0);
+              for (int ks = 0; ks < KSTEPS; ++ks)
+                sc[s][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], S[s].qf[ks], sc[s][c], 0, 0, 0);
             }
-          } else {
+          }
+          // ---- phase 2: softmax over the group's scores
+          bf16x8 pf[NS][NP > 0 ? NP : 1];
+          bf16x4 pt[NS];
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            if (!sact[s]) {
+              // a free slot: its (ignored) products run on zero weights
+#pragma unroll
+              for (int pi = 0; pi < (NP > 0 ? NP : 1); ++pi) pf[s][pi] = bf16x8{};
+              pt[s] = bf16x4{};
+              continue;
+            }
+            float mx = kNegInf;
+#pragma unroll
+            for (int c = 0; c < NK; ++c)
+              mx = fmaxf(mx, fmaxf(fmaxf(sc[s][c][0], sc[s][c][1]), fmaxf(sc[s][c][2], sc[s][c][3])));
+            mx = xmax4(mx);
+            // the reference max moves (and the running output is rescaled)
+            // only when a score exceeds it by more than kRescale
+            if (__builtin_amdgcn_ballot_w64(mx > S[s].m + kRescale) != 0) {
+              const float mn = fmaxf(S[s].m, mx);
+              const float alpha = S[s].m == kNegInf ? 0.f : __builtin_amdgcn_exp2f((S[s].m - mn) * kLog2e);
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) S[s].acc[mt] *= alpha;
+              S[s].accl *= alpha;
+              S[s].m = mn;
+            }
+            const float mb = S[s].m == kNegInf ? 0.f : S[s].m * kLog2e;
+#pragma unroll
+            for (int c = 0; c < NK; ++c) {
+              float p[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s][c][r], kLog2e, -mb));
+              if (c == NK - 1 && ODD) {
+                pt[s] = bf16x4{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pf[s][c >> 1][4 * (c & 1) + r] = (__bf16)p[r];
+              }
+            }
+          }
+          // ---- phase 3: O^T += V^T . P^T, every tile pair of the group
+#pragma unroll
+          for (int pi = 0; pi < NP; ++pi) {
             bf16x8 vf[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-              vf[mt] = cat8(load_vt(lv, vofs[mt] + 32 * bi * RB), load_vt(lv, vofs[mt] + (32 * bi + 16) * RB));
+              vf[mt] = cat8(load_vt(lv, vofs[mt] + gofs + 32 * pi * RB),
+                            load_vt(lv, vofs[mt] + gofs + (32 * pi + 16) * RB));
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-              if (!sact[s]) continue;
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt)
-                S[s].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[mt], pf[s][j], S[s].acc[mt], 0, 0, 0);
+                S[s].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[mt], pf[s][pi], S[s].acc[mt], 0, 0, 0);
+              S[s].accl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pf[s][pi], S[s].accl, 0, 0, 0);
+            }
+          }
+          if (ODD) {
+            s16x4 vt[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) vt[mt] = load_vt(lv, vofs[mt] + gofs + 16 * (NK - 1) * RB);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              const s16x4 pb = __builtin_bit_cast(s16x4, pt[s]);
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                S[s].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[mt], pb, S[s].acc[mt], 0, 0, 0);
+              S[s].accl = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kOnes4, pb, S[s].accl, 0, 0, 0);
             }
           }
         }
-        // keep the scheduler from hoisting the next group's operand reads
-        // above this one, which would hold every group's fragments at once
-        if (NGRP > 1) __builtin_amdgcn_sched_barrier(0);
       }
-    }
 
-    // retire this wave's query planes whose window ends here
-    while (jlo <= jhi && win_start(tq(jlo), KT, T) + KT - 1 == tp) {
-      const int sl = jlo % NS;
-      uint16_t* op = a.o + bbase + (int64_t)tq(jlo) * plane + qtok;
-      if (active) {
+      // retire this wave's query planes whose window ends here; the output
+      // waits in registers for the next barrier (a second one in the same
+      // plane is stored at once)
+      while (jlo <= jhi && win_start(tq(jlo), KT, T) + KT - 1 == tp) {
+        const int sl = jlo % NS;
+        if (active) {
+          if (pend_on && qvalid) store_out<MT>(pend_p, pend, g);
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-          if (s == sl) slot_finish(S[s], op, g, qvalid);
+          for (int s = 0; s < NS; ++s)
+            if (s == sl) pack_out<HD>(S[s], pend);
+          pend_p = a.o + bbase + (int64_t)tq(jlo) * plane + qtok;
+          pend_on = true;
+        }
+        ++jlo;
       }
-      ++jlo;
-    }
-    // one buffer: every wave must be done with plane tp before it is refilled
-    if (NBUF == 1 && tp + 1 < p1) {
-      __syncthreads();
-      issue_stage(tp + 1, 0);
+      // one buffer: every wave must be done with plane tp before it is refilled
+      if (NBUF == 1 && nxt >= 0) {
+        __syncthreads();
+        issue_stage(nxt, 0);
+      }
     }
   }
+  if (pend_on && qvalid) store_out<MT>(pend_p, pend, g);
 }
 
 // ------------------------------------------------------------------ launch
-template <int HD, int QH, int QW, int WH, int WT, int NS, int MAXB, int NBUF, int SB>
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF>
 int launch_cfg(const RollArgs& a, const Launch& l, hipStream_t stream) {
-  auto kern = na3d_fwd_roll_kernel<HD, QH, QW, WH, WT, NS, MAXB, NBUF, SB>;
+  auto kern = na3d_fwd_roll_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF>;
   if (l.lds_bytes > 64 * 1024 &&
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, l.lds_bytes) != hipSuccess)
@@ -480,11 +607,15 @@ int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s) {
   a.tiles_h = l.tiles_h;
   a.tiles_w = l.tiles_w;
   a.tc = l.tile_t;
+  a.ta = l.ta;
+  a.tz = l.tz;
+  a.nruns = l.nruns;
+  a.rpw = l.rpw;
   a.lds_rows = l.lds_rows;
   if (l.variant < 0 || l.variant >= kNumRollVariants || kRollVariants[l.variant].hd != hd) return -1;
   switch (l.variant) {
-#define NA3D_ROLL_CASE(i, HD, QH, QW, WH, WT, NS, MAXB, NBUF, SB) \
-  case i: return launch_cfg<HD, QH, QW, WH, WT, NS, MAXB, NBUF, SB>(a, l, s);
+#define NA3D_ROLL_CASE(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF) \
+  case i: return launch_cfg<HD, QH, QW, WH, WT, NS, NK, NG, NBUF>(a, l, s);
     NA3D_ROLL_VARIANTS(NA3D_ROLL_CASE)
 #undef NA3D_ROLL_CASE
     default: return -1;

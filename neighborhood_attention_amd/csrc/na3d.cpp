@@ -43,13 +43,31 @@ int check_sizes(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int 
   return NA3D_OK;
 }
 
-// Most query planes one wave holds at a time: a run [t0, t0 + tc) is split
-// over WT waves (wave r owns t0 + r, t0 + r + WT, ...); count, over all key
-// planes, the owned query planes whose window contains that key plane.
-int max_active_per_wave(int T, int KT, int tc, int wt) {
+// Query-plane runs along T: an optional first run [0, ta) (the planes whose
+// window is [0, KT)), middle runs of tc planes over [ta, tz), and an optional
+// last run [tz, T) (the planes whose window is [T - KT, T)).
+struct Runs {
+  int ta, tz, tc;
+};
+
+int run_count(int T, const Runs& r) {
+  return (r.ta > 0) + (r.tz > r.ta ? ceil_div(r.tz - r.ta, r.tc) : 0) + (r.tz < T);
+}
+
+// Calls f(t0, t1) for every run.
+template <class F>
+void for_runs(int T, const Runs& r, F f) {
+  if (r.ta > 0) f(0, r.ta);
+  for (int t0 = r.ta; t0 < r.tz; t0 += r.tc) f(t0, std::min(t0 + r.tc, r.tz));
+  if (r.tz < T) f(r.tz, T);
+}
+
+// Most query planes one wave holds at a time: in a run [t0, t1) wave r of WT
+// owns t0 + r, t0 + r + WT, ...; count, over all key planes of the run, the
+// owned query planes whose window contains that key plane.
+int max_active_per_wave(int T, int KT, const Runs& runs, int wt) {
   int best = 0;
-  for (int t0 = 0; t0 < T; t0 += tc) {
-    const int t1 = std::min(t0 + tc, T);
+  for_runs(T, runs, [&](int t0, int t1) {
     const int p0 = win_start(t0, KT, T), p1 = win_start(t1 - 1, KT, T) + KT;
     for (int r = 0; r < wt; ++r)
       for (int tp = p0; tp < p1; ++tp) {
@@ -60,8 +78,52 @@ int max_active_per_wave(int T, int KT, int tc, int wt) {
         }
         best = std::max(best, c);
       }
-  }
+  });
   return best;
+}
+
+// K/V planes staged per spatial tile over all runs, and the most in one run.
+void staged_planes(int T, int KT, const Runs& runs, int* total, int* most) {
+  *total = 0;
+  *most = 0;
+  for_runs(T, runs, [&](int t0, int t1) {
+    const int n = win_start(t1 - 1, KT, T) + KT - win_start(t0, KT, T);
+    *total += n;
+    *most = std::max(*most, n);
+  });
+}
+
+// Runs for a rolling variant with wt waves along T and ns slots per wave.
+// tile_t > 0 fixes the middle run length.  Both layouts are tried: with the
+// shared-window planes split off into runs of their own, and without; the
+// feasible one that stages fewer planes wins.
+bool choose_runs(int T, int KT, int wt, int ns, int tile_t, Runs* out) {
+  int ta = 0;
+  while (ta < T && win_start(ta, KT, T) == 0) ++ta;
+  int tz = T;
+  while (tz > 0 && win_start(tz - 1, KT, T) == T - KT) --tz;
+  bool found = false;
+  int best_cost = 0;
+  for (int split = 1; split >= 0; --split) {
+    Runs r;
+    r.ta = split ? ta : 0;
+    r.tz = split ? std::max(tz, ta) : T;
+    if (split && (ta >= T || r.tz <= 0)) continue;  // one shared window: nothing to split
+    const int span = std::max(r.tz - r.ta, 1);
+    int tc = tile_t > 0 ? std::min(tile_t, span) : span;
+    r.tc = tc;
+    if (tile_t <= 0)
+      while (tc > 1 && max_active_per_wave(T, KT, r, wt) > ns) r.tc = --tc;
+    if (max_active_per_wave(T, KT, r, wt) > ns) continue;
+    int total, most;
+    staged_planes(T, KT, r, &total, &most);
+    if (!found || total < best_cost) {
+      found = true;
+      best_cost = total;
+      *out = r;
+    }
+  }
+  return found;
 }
 
 bool plan_general(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, Launch* l) {
@@ -72,6 +134,10 @@ bool plan_general(int B, int T, int H, int W, int NH, int HD, int KT, int KH, in
   l->tile_h = BH;
   l->tile_w = BW;
   l->tiles_t = T;
+  l->ta = 0;
+  l->tz = T;
+  l->nruns = T;
+  l->rpw = 1;
   l->tiles_h = ceil_div(H, BH);
   l->tiles_w = ceil_div(W, BW);
   l->wgs = (int64_t)B * NH * T * l->tiles_h * l->tiles_w;
@@ -91,61 +157,88 @@ bool plan_roll(int v, int B, int T, int H, int W, int NH, int HD, int KT, int KH
   if (v < 0 || v >= kNumRollVariants) return false;
   const RollVariant& rv = kRollVariants[v];
   if (rv.hd != HD) return false;
+  // staging offsets are 32-bit byte offsets within one K/V plane
+  if ((int64_t)H * W * NH * HD * 2 >= ((int64_t)1 << 32)) return false;
   const int BH = rv.wh * rv.qh;
   const int hwd_max = std::min(rv.qw + KW - 1, W);
   const int un_max = std::min(rv.qh + KH - 1, H) * hwd_max;
-  if (un_max / 32 > rv.maxb) return false;
+  const int gk = 16 * rv.nk;
+  const int ngrp = ceil_div(un_max, gk);
+  if (ngrp > rv.ng) return false;
   const int halo_max = std::min(BH + KH - 1, H) * hwd_max;
+  // every wave's read window of ngrp * gk rows fits in a buffer
+  const int rows = std::max(halo_max, ngrp * gk);
   // K and V rows of HD*2 bytes, in one or two plane buffers
-  const int64_t lds = 2LL * rv.nbuf * (halo_max + kPadRows) * (HD * 2);
+  const int64_t lds = 2LL * rv.nbuf * rows * (HD * 2);
   if (lds > kMaxLdsBytes) return false;
   const int tiles_h = ceil_div(H, BH), tiles_w = ceil_div(W, rv.qw);
   const int64_t spatial = (int64_t)B * NH * tiles_h * tiles_w;
-  int tc;
-  if (tile_t > 0) {
-    tc = std::min(tile_t, T);
-    if (max_active_per_wave(T, KT, tc, rv.wt) > rv.ns) return false;
-  } else {
-    // longest run that fits the slots, shortened while the grid is too small
-    tc = T;
-    while (tc > 1 && max_active_per_wave(T, KT, tc, rv.wt) > rv.ns) --tc;
-    if (max_active_per_wave(T, KT, tc, rv.wt) > rv.ns) return false;
-    while (tc > rv.wt && spatial * ceil_div(T, tc) < kTargetWorkgroups) tc = ceil_div(tc, 2);
+  Runs r;
+  if (!choose_runs(T, KT, rv.wt, rv.ns, tile_t, &r)) return false;
+  if (tile_t <= 0) {
+    // shorter middle runs while the grid is too small to fill the chip
+    while (r.tc > rv.wt && spatial * run_count(T, r) < kTargetWorkgroups) {
+      Runs s = r;
+      s.tc = ceil_div(r.tc, 2);
+      if (max_active_per_wave(T, KT, s, rv.wt) > rv.ns) break;
+      r = s;
+    }
   }
+  int total, most;
+  staged_planes(T, KT, r, &total, &most);
+  // a workgroup streams several consecutive runs (one set-up, and the next
+  // run's first plane is fetched during the last plane of the previous one)
+  // as long as the grid keeps enough workgroups
+  const int nruns = run_count(T, r);
+  const int groups = (int)std::min<int64_t>(nruns, std::max<int64_t>(1, (kTargetWorkgroups + spatial - 1) / spatial));
+  const int rpw = ceil_div(nruns, groups);
   l->family = 2;
   l->variant = v;
-  l->tile_t = tc;
+  l->tile_t = r.tc;
   l->tile_h = BH;
   l->tile_w = rv.qw;
-  l->tiles_t = ceil_div(T, tc);
+  l->tiles_t = ceil_div(nruns, rpw);
+  l->nruns = nruns;
+  l->rpw = rpw;
   l->tiles_h = tiles_h;
   l->tiles_w = tiles_w;
+  l->ta = r.ta;
+  l->tz = r.tz;
   l->wgs = spatial * l->tiles_t;
   l->threads = kWave * rv.wh * rv.wt;
-  l->lds_rows = halo_max + kPadRows;
+  l->lds_rows = rows;
   l->lds_bytes = (int)lds;
-  l->planes = std::min(T, win_start(std::min(tc, T) - 1, KT, T) + KT);
+  l->planes = std::min(rpw, nruns) == 1 ? most : total;  // upper bound for run groups
   return l->wgs <= 0x7fffffff;
 }
 
-// Preferred rolling instantiations, best first, by head dimension and window
-// area (large windows need big unions and favour single-buffered staging).
+// Preferred rolling instantiations, best first (from measured sweeps), by
+// head dimension and by the union of one 2x8 query block's windows; the first
+// whose static limits fit the sizes wins.
 int pick_roll(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, Launch* l) {
-  static const int p16[] = {0};
-  static const int p32[] = {1};
-  static const int p64_small[] = {2, 3, 4, 5, 6};
-  static const int p64_large[] = {6, 7, 8};
-  static const int p128[] = {9, 10, 11};
-  static const int p256[] = {12};
+  static const int p16[] = {11};
+  static const int p32[] = {12};
+  static const int p64_small[] = {28, 8, 26, 21, 20, 9};   // union <= 64 keys
+  static const int p64_mid[] = {26, 21, 20, 1, 9, 10};     // union <= 112 keys
+  static const int p64_large[] = {5, 10, 22, 6, 7, 9};     // larger windows
+  static const int p128[] = {25, 15, 14, 13, 16, 29};
+  static const int p256[] = {17};
+  const int un28 = std::min(2 + KH - 1, H) * std::min(8 + KW - 1, W);
   const int* pref;
   int np;
   switch (HD) {
     case 16: pref = p16; np = 1; break;
     case 32: pref = p32; np = 1; break;
     case 64:
-      if (KH * KW <= 64) { pref = p64_small; np = 5; } else { pref = p64_large; np = 3; }
+      if (un28 <= 64) {
+        pref = p64_small; np = (int)(sizeof(p64_small) / sizeof(int));
+      } else if (un28 <= 112) {
+        pref = p64_mid; np = (int)(sizeof(p64_mid) / sizeof(int));
+      } else {
+        pref = p64_large; np = (int)(sizeof(p64_large) / sizeof(int));
+      }
       break;
-    case 128: pref = p128; np = 3; break;
+    case 128: pref = p128; np = (int)(sizeof(p128) / sizeof(int)); break;
     default: pref = p256; np = 1; break;
   }
   for (int i = 0; i < np; ++i)
@@ -179,6 +272,8 @@ void fill_plan(const Launch& l, int* plan) {
   plan[5] = l.threads;
   plan[6] = l.lds_bytes;
   plan[7] = l.planes;
+  plan[8] = l.variant;
+  plan[9] = l.tiles_t;
 }
 
 // gfx950 check, cached per device (0 unknown, 1 yes, -1 no)
@@ -221,7 +316,7 @@ using namespace na3d;
 
 extern "C" {
 
-int na3d_abi_version(void) { return 1; }
+int na3d_abi_version(void) { return 2; }
 
 int na3d_num_variants(void) { return kNumRollVariants; }
 

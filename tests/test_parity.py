@@ -216,10 +216,10 @@ def variant_cases():
     lib = na.load()
     for var in range(na.num_variants()):
         for hd, (shape, ks) in table.items():
-            buf = (ctypes.c_int * 8)()
+            buf = (ctypes.c_int * 10)()
             if lib.na3d_plan_config(*shape, *ks, 2, var, 0, buf) == 0:
                 cases.append((2, var, shape, ks))
-        buf = (ctypes.c_int * 8)()
+        buf = (ctypes.c_int * 10)()
         if lib.na3d_plan_config(*big[0], *big[1], 2, var, 0, buf) == 0:
             cases.append((2, var) + big)
     return cases
@@ -244,6 +244,6 @@ def test_rolling_run_lengths(tile_t):
     q, k, v = inputs_on_gpu(shape, 90)
     p = na.plan(shape, ks)
     assert p["family"] == 2
-    out = na.fwd(q, k, v, ks, config=(2, 2, tile_t))
+    out = na.fwd(q, k, v, ks, config=(2, p["variant"], tile_t))
     torch.cuda.synchronize()
     compare(to_np(out), oracle.fwd(q.cpu(), k.cpu(), v.cpu(), ks), "run length %d" % tile_t)
