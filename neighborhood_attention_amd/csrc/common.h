@@ -123,7 +123,11 @@ struct Launch {
   X(26, 64, 2, 8, 2, 2, 2, 7, 1, 2)         \
   X(27, 64, 2, 8, 4, 1, 3, 4, 2, 1)         \
   X(28, 64, 2, 8, 2, 1, 3, 4, 2, 2)         \
-  X(29, 128, 2, 8, 2, 2, 2, 4, 2, 1)
+  X(29, 128, 2, 8, 2, 2, 2, 4, 2, 1)        \
+  X(30, 64, 2, 8, 1, 4, 1, 4, 2, 1)         \
+  X(31, 64, 2, 8, 1, 4, 1, 4, 2, 2)         \
+  X(32, 64, 4, 4, 1, 4, 1, 4, 2, 1)         \
+  X(33, 128, 2, 8, 1, 4, 1, 4, 2, 1)
 
 struct RollVariant {
   int hd, qh, qw, wh, wt, ns, nk, ng, nbuf;

@@ -27,14 +27,15 @@
 // in the middle runs a wave's consecutive query planes (WT apart) have
 // disjoint windows and WT = KT keeps every wave busy on every key plane.
 //
-// Per key plane a wave reads a window of 16*NK*ngrp staged rows that covers
-// its union (shifted down where it would pass the end of the buffer), in
-// ngrp groups of NK 16-key tiles.  Each group runs three phases, each over
-// all of its tiles and all active query planes, with no data-dependent
-// branches inside, so the MFMAs and exponentials of a phase are independent:
-//   S^T = K . Q^T + bias    bf16 MFMA 16x16x32; bias (0 or -inf) is the
-//                           window mask, computed once per wave and fed in
-//                           as the accumulator input, so masking costs no VALU
+// Per key plane a wave reads a window of 16*NK*NG staged rows that covers
+// its union (shifted down where it would pass the end of the buffer), as NG
+// groups of NK 16-key tiles.  A (group, query plane) unit takes three steps;
+// units run as a software pipeline, so one unit's exponentials share a
+// branch-free region with the next unit's score MFMAs and the previous
+// unit's P.V MFMAs:
+//   S^T = K . Q^T + mask    bf16 MFMA 16x16x32, seeded with the window mask
+//                           (0 or -2^100): one MFMA per tile of the mask,
+//                           kept as bf16 in registers, against the identity
 //   softmax                 one exact max over the group's scores, one
 //                           rescale of the running output, then exp2
 //   O^T += V^T . P^T        bf16 MFMA 16x16x32 per pair of tiles (16x16x16
@@ -58,7 +59,11 @@ constexpr float kNegInf = -__builtin_inff();
 // Natural-log headroom before the reference max is moved: unnormalised
 // weights stay below e^8 (about 3000), far inside bf16 and fp32 range.
 constexpr float kRescale = 8.f;
-constexpr uint32_t kBf16NegInf = 0xff80u;
+// Score of a key outside a query's window: -2^100, finite so that the mask
+// MFMA against the identity has no -inf * 0 terms, and far below any real
+// score, so exp2 of it relative to a real reference max is exactly 0.
+constexpr uint32_t kMaskBits = 0xf180u;   // bf16 -2^100
+constexpr float kRealScore = -1.0e27f;    // scores below this are masked ones
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left free (gfx9 layout)
 constexpr int kWaitVm0 = 0x0f70;
 
@@ -200,13 +205,6 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
 }
 
-// Window-mask bias of the 4 scores of a 16-key tile, packed as bf16 pairs
-// (0 or -inf), expanded to the f32x4 accumulator input.
-__device__ __forceinline__ f32x4 unpack_bias(const uint32_t (&w)[2]) {
-  return f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
-               __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xffff0000u)};
-}
-
 template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF>
 __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const RollArgs a) {
   static_assert(QH * QW == 16, "a wave owns 16 queries");
@@ -225,7 +223,6 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
   // weights of each query, already reduced over its four lanes
   const bf16x8 kOnes8 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
-  const s16x4 kOnes4 = {0x3f80, 0x3f80, 0x3f80, 0x3f80};
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int buf_bytes = a.lds_rows * RB;  // one K or V plane buffer
@@ -289,43 +286,79 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
   const int ash = win_start(qhc, KH, H);
   const int asw = win_start(qwc, KW, W);
   // union of the block's windows = staged rows [base, base + un); the wave
-  // reads rows [rb, rb + ngrp * GK), which hold the union and stay in the buffer
+  // reads rows [rb, rb + NG * GK), which hold the union (the host checks
+  // NG * GK >= un) and stay in the buffer (lds_rows >= NG * GK)
   const int uh0 = bh0 < H ? win_start(bh0, KH, H) : hh0;
-  const int un = active ? (win_start(bh1, KH, H) + KH - uh0) * hwd : 0;
   const int base = (uh0 - hh0) * hwd;
-  const int ngrp = (un + GK - 1) / GK;
-  const int rb = max(0, min(base, a.lds_rows - ngrp * GK));
+  const int rb = max(0, min(base, a.lds_rows - NG * GK));
 
-  // ---- window masks of every tile, packed as bf16 pairs (0 = in window)
-  const float inv_hwd = 1.f / (float)hwd;
-  auto key_out = [&](int r) -> uint32_t {
-    if (!qvalid || r >= halo_rows) return kBf16NegInf;
-    int uh = (int)((float)r * inv_hwd);
-    int uw = r - uh * hwd;
-    if (uw < 0) { --uh; uw += hwd; }
-    if (uw >= hwd) { ++uh; uw -= hwd; }
-    const bool in = (unsigned)(hh0 + uh - ash) < (unsigned)KH &&
-                    (unsigned)(hw0 + uw - asw) < (unsigned)KW;
-    return in ? 0u : kBf16NegInf;
-  };
-  uint32_t bias[NG][NK][2];
+  // ---- window masks.  For tile c of group gi, lane (q16, g) holds the A
+  // operand of a 16x16x16 MFMA against the identity: for the key in MFMA row
+  // q16 (the same key its K operand row holds) and the block's queries
+  // 4g .. 4g+3, 0 (in window) or -2^100 (out), as bf16 pairs.  The product
+  // lands in the S^T accumulator layout and seeds the score MFMAs.
+  int ah[4], aw[4];  // window starts of queries 4g + j, relative to the halo
 #pragma unroll
-  for (int gi = 0; gi < NG; ++gi)
+  for (int j = 0; j < 4; ++j) {
+    const int qi = 4 * g + j;
+    const int qhj = bh0 + qi / QW, qwj = w0 + qi % QW;
+    const bool ok = active && qhj < H && qwj < W;
+    ah[j] = ok ? win_start(qhj, KH, H) - hh0 : -(1 << 20);
+    aw[j] = win_start(min(qwj, W - 1), KW, W) - hw0;
+  }
+  const int kp = key_perm(HD, q16);
+  constexpr int NKP = (NK + 1) / 2;  // tile pairs per group
+  uint4 mk[NG][NKP];                 // tiles 2p (x, y) and 2p + 1 (z, w)
+  {
+    // halo coordinates of this lane's key row, advanced 16 rows per tile
+    int r = rb + kp;
+    int uh = r / hwd, uw = r - (r / hwd) * hwd;
+    const int dh = 16 / hwd, dw = 16 % hwd;
 #pragma unroll
-    for (int c = 0; c < NK; ++c)
+    for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        // score slot r of a tile holds key key_perm(4g + r) of the tile
-        const int r0 = rb + GK * gi + 16 * c;
-        bias[gi][c][i] = key_out(r0 + key_perm(HD, 4 * g + 2 * i)) |
-                         (key_out(r0 + key_perm(HD, 4 * g + 2 * i + 1)) << 16);
+      for (int c = 0; c < NK; ++c) {
+        uint32_t bits[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool in = r < halo_rows && (unsigned)(uh - ah[j]) < (unsigned)KH &&
+                          (unsigned)(uw - aw[j]) < (unsigned)KW;
+          bits[j] = in ? 0u : kMaskBits;
+        }
+        const uint32_t w0 = bits[0] | (bits[1] << 16), w1 = bits[2] | (bits[3] << 16);
+        if (c & 1) {
+          mk[gi][c >> 1].z = w0;
+          mk[gi][c >> 1].w = w1;
+        } else {
+          mk[gi][c >> 1].x = w0;
+          mk[gi][c >> 1].y = w1;
+          if (c == NK - 1) mk[gi][c >> 1].z = mk[gi][c >> 1].w = 0u;
+        }
+        r += 16;
+        uh += dh;
+        uw += dw;
+        if (uw >= hwd) {
+          uw -= hwd;
+          ++uh;
+        }
       }
+  }
+  // B operands of the mask MFMA (16x16x32): lane (q16, g) holds rows
+  // 8g .. 8g+7 of column q16.  Row 8g + i carries query 4g + (i & 3) of the
+  // even tile of a pair (i < 4) or of the odd one (i >= 4); the identity
+  // picks one of the two
+  bf16x8 ident_e, ident_o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool hit = 4 * g + (i & 3) == q16;
+    ident_e[i] = (__bf16)((hit && i < 4) ? 1.f : 0.f);
+    ident_o[i] = (__bf16)((hit && i >= 4) ? 1.f : 0.f);
+  }
 
   // ---- operand offsets inside one plane buffer; tiles add multiples of 16
   // rows, which leave the swizzle unchanged
   // K operand: lane (q16, g) holds key kp of a tile; V operand (transpose
   // read): lane (4j + a) of group g addresses key vp = key_perm(4g + j)
-  const int kp = key_perm(HD, q16);
   const int vp = key_perm(HD, 4 * g + (q16 >> 2));
   int kofs[KSTEPS], vofs[MT];
 #pragma unroll
@@ -457,18 +490,20 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
       if (active && jhi >= jlo) {
         const unsigned char* lk = smem + (NBUF == 2 ? (st & 1) : 0) * 2 * buf_bytes;
         const unsigned char* lv = lk + buf_bytes;
-        bool sact[NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) sact[s] = ((s - jlo % NS + NS) % NS) < (jhi - jlo + 1);
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          if (gi >= ngrp) break;
+        // Work unit u = (group u / NS, slot u % NS).  Units run as a software
+        // pipeline: while unit u's weights are exponentiated (VALU), the
+        // scores of unit u+1 and the P.V products of unit u-1 (MFMA) are in
+        // flight, all in one branch-free region.  Free slots run too (on
+        // stale Q; admission resets the slot), so the regions stay
+        // branch-free; only the rare rescale of the running output branches.
+        constexpr int NU = NG * NS;
+        constexpr int NPP = (NK + 1) / 2;  // P operands (tile pairs) per unit
+        f32x4 sc[2][NK];
+        bf16x8 pf[2][NPP];
+        // S^T = K . Q^T + mask for every tile of unit u
+        auto unit_scores = [&](int u, f32x4 (&out)[NK]) __attribute__((always_inline)) {
+          const int gi = u / NS, sl = u % NS;
           const int gofs = GK * gi * RB;
-          // The MFMAs of phases 1 and 3 also run for free slots (on zero
-          // weights and stale Q; admission resets the slot), so that these
-          // phases hold no branches and their operand reads issue early.
-          // ---- phase 1: S^T = K . Q^T + mask, every tile of the group
-          f32x4 sc[NS][NK];
 #pragma unroll
           for (int c = 0; c < NK; ++c) {
             bf16x8 kf[KSTEPS];
@@ -477,86 +512,99 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
               kf[ks] = (32 * ks + 8 * g < HD)
                            ? *reinterpret_cast<const bf16x8*>(lk + kofs[ks] + gofs + 16 * c * RB)
                            : bf16x8{};
-            const f32x4 bc = unpack_bias(bias[gi][c]);
+            // the window mask of tile c: the pair's mask against the identity
+            // half that selects tile c (same MFMA kind as the score chain,
+            // whose accumulator it seeds)
+            out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, mk[gi][c >> 1]), (c & 1) ? ident_o : ident_e,
+                f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              sc[s][c] = bc;
-#pragma unroll
-              for (int ks = 0; ks < KSTEPS; ++ks)
-                sc[s][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], S[s].qf[ks], sc[s][c], 0, 0, 0);
-            }
+            for (int ks = 0; ks < KSTEPS; ++ks)
+              out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], S[sl].qf[ks], out[c], 0, 0, 0);
           }
-          // ---- phase 2: softmax over the group's scores
-          bf16x8 pf[NS][NP > 0 ? NP : 1];
-          bf16x4 pt[NS];
+        };
+        // max of unit u's scores; the reference max moves (and the running
+        // output is rescaled) only when a real score (not a mask value)
+        // exceeds it by more than kRescale
+        auto unit_max = [&](int u, const f32x4 (&in)[NK]) __attribute__((always_inline)) {
+          const int sl = u % NS;
+          float mx = kNegInf;
 #pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            if (!sact[s]) {
-              // a free slot: its (ignored) products run on zero weights
+          for (int c = 0; c < NK; ++c)
+            mx = fmaxf(mx, fmaxf(fmaxf(in[c][0], in[c][1]), fmaxf(in[c][2], in[c][3])));
+          mx = xmax4(mx);
+          if (__builtin_amdgcn_ballot_w64(mx > S[sl].m + kRescale && mx > kRealScore) != 0) {
+            const float mn = mx > kRealScore ? fmaxf(S[sl].m, mx) : S[sl].m;
+            const float alpha = S[sl].m == kNegInf ? 0.f : __builtin_amdgcn_exp2f((S[sl].m - mn) * kLog2e);
 #pragma unroll
-              for (int pi = 0; pi < (NP > 0 ? NP : 1); ++pi) pf[s][pi] = bf16x8{};
-              pt[s] = bf16x4{};
-              continue;
-            }
-            float mx = kNegInf;
-#pragma unroll
-            for (int c = 0; c < NK; ++c)
-              mx = fmaxf(mx, fmaxf(fmaxf(sc[s][c][0], sc[s][c][1]), fmaxf(sc[s][c][2], sc[s][c][3])));
-            mx = xmax4(mx);
-            // the reference max moves (and the running output is rescaled)
-            // only when a score exceeds it by more than kRescale
-            if (__builtin_amdgcn_ballot_w64(mx > S[s].m + kRescale) != 0) {
-              const float mn = fmaxf(S[s].m, mx);
-              const float alpha = S[s].m == kNegInf ? 0.f : __builtin_amdgcn_exp2f((S[s].m - mn) * kLog2e);
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt) S[s].acc[mt] *= alpha;
-              S[s].accl *= alpha;
-              S[s].m = mn;
-            }
-            const float mb = S[s].m == kNegInf ? 0.f : S[s].m * kLog2e;
-#pragma unroll
-            for (int c = 0; c < NK; ++c) {
-              float p[4];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s][c][r], kLog2e, -mb));
-              if (c == NK - 1 && ODD) {
-                pt[s] = bf16x4{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
-              } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pf[s][c >> 1][4 * (c & 1) + r] = (__bf16)p[r];
-              }
-            }
+            for (int mt = 0; mt < MT; ++mt) S[sl].acc[mt] *= alpha;
+            S[sl].accl *= alpha;
+            S[sl].m = mn;
           }
-          // ---- phase 3: O^T += V^T . P^T, every tile pair of the group
+        };
+        // weights of unit u as bf16 P^T operands (an odd last tile padded
+        // with zero weights)
+        auto unit_exp = [&](int u, const f32x4 (&in)[NK], bf16x8 (&out)[NPP]) __attribute__((always_inline)) {
+          const int sl = u % NS;
+          const float mb = S[sl].m == kNegInf ? 0.f : S[sl].m * kLog2e;
 #pragma unroll
-          for (int pi = 0; pi < NP; ++pi) {
-            bf16x8 vf[MT];
+          for (int c = 0; c < NK; ++c) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              vf[mt] = cat8(load_vt(lv, vofs[mt] + gofs + 32 * pi * RB),
-                            load_vt(lv, vofs[mt] + gofs + (32 * pi + 16) * RB));
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-                S[s].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[mt], pf[s][pi], S[s].acc[mt], 0, 0, 0);
-              S[s].accl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pf[s][pi], S[s].accl, 0, 0, 0);
-            }
+            for (int r = 0; r < 4; ++r)
+              out[c >> 1][4 * (c & 1) + r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(in[c][r], kLog2e, -mb));
           }
           if (ODD) {
-            s16x4 vt[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) vt[mt] = load_vt(lv, vofs[mt] + gofs + 16 * (NK - 1) * RB);
+            for (int r = 4; r < 8; ++r) out[NPP - 1][r] = (__bf16)0.f;
+          }
+        };
+        // O^T += V^T . P^T and the denominator for unit u
+        auto unit_pv = [&](int u, const bf16x8 (&in)[NPP]) __attribute__((always_inline)) {
+          const int gi = u / NS, sl = u % NS;
+          const int gofs = GK * gi * RB;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              const s16x4 pb = __builtin_bit_cast(s16x4, pt[s]);
+          for (int pi = 0; pi < NPP; ++pi) {
+            bf16x8 vf[MT];
 #pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-                S[s].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[mt], pb, S[s].acc[mt], 0, 0, 0);
-              S[s].accl = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kOnes4, pb, S[s].accl, 0, 0, 0);
+            for (int mt = 0; mt < MT; ++mt) {
+              const s16x4 lo = load_vt(lv, vofs[mt] + gofs + 32 * pi * RB);
+              // the padded half of an odd last tile re-reads the same rows
+              const s16x4 hi = (ODD && pi == NPP - 1) ? lo : load_vt(lv, vofs[mt] + gofs + (32 * pi + 16) * RB);
+              vf[mt] = cat8(lo, hi);
             }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              S[sl].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[mt], in[pi], S[sl].acc[mt], 0, 0, 0);
+            S[sl].accl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, in[pi], S[sl].accl, 0, 0, 0);
+          }
+        };
+        // keeps unit u's weights computed where they stand in the pipeline
+        // (the compiler would otherwise sink them past the next branch)
+        auto pin = [&](bf16x8 (&w)[NPP]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int pi = 0; pi < NPP; ++pi) asm volatile("" : "+v"(w[pi]));
+        };
+        unit_scores(0, sc[0]);
+        unit_max(0, sc[0]);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          unit_exp(u, sc[u & 1], pf[u & 1]);
+          if (u + 1 < NU) unit_scores(u + 1, sc[(u + 1) & 1]);
+          if (NS >= 2) {
+            // unit u + 1 belongs to another query plane: the previous unit's
+            // products can share this region
+            if (u >= 1) unit_pv(u - 1, pf[(u - 1) & 1]);
+            pin(pf[u & 1]);
+            if (u + 1 < NU) unit_max(u + 1, sc[(u + 1) & 1]);
+          } else {
+            pin(pf[u & 1]);
+            // one query plane: its products must land before the next
+            // unit's max may rescale the running output
+            unit_pv(u, pf[u & 1]);
+            if (u + 1 < NU) unit_max(u + 1, sc[(u + 1) & 1]);
           }
         }
+        if (NS >= 2) unit_pv(NU - 1, pf[(NU - 1) & 1]);
       }
 
       // retire this wave's query planes whose window ends here; the output

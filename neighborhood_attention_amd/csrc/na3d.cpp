@@ -163,11 +163,10 @@ bool plan_roll(int v, int B, int T, int H, int W, int NH, int HD, int KT, int KH
   const int hwd_max = std::min(rv.qw + KW - 1, W);
   const int un_max = std::min(rv.qh + KH - 1, H) * hwd_max;
   const int gk = 16 * rv.nk;
-  const int ngrp = ceil_div(un_max, gk);
-  if (ngrp > rv.ng) return false;
+  if (un_max > rv.ng * gk) return false;
   const int halo_max = std::min(BH + KH - 1, H) * hwd_max;
-  // every wave's read window of ngrp * gk rows fits in a buffer
-  const int rows = std::max(halo_max, ngrp * gk);
+  // every wave's read window of ng * gk rows fits in a buffer
+  const int rows = std::max(halo_max, rv.ng * gk);
   // K and V rows of HD*2 bytes, in one or two plane buffers
   const int64_t lds = 2LL * rv.nbuf * rows * (HD * 2);
   if (lds > kMaxLdsBytes) return false;
