@@ -92,50 +92,55 @@ struct Launch {
 // Instantiations of the rolling family: index, head dim, query block
 // (QH x QW = 16 queries per wave), wave grid (WH block rows x WT query-plane
 // phases), query-plane slots per wave, 16-key tiles per softmax group, most
-// groups a wave's window union may need, and staged plane buffers (1 or 2).
+// groups a wave's window union may need, staged plane buffers (1 or 2), and
+// the waves per SIMD the register allocation must leave room for (0 = the
+// compiler's choice; 4 caps it at 128 VGPRs).
 #define NA3D_ROLL_VARIANTS(X)               \
-  X(0, 64, 2, 8, 1, 3, 1, 7, 1, 2)          \
-  X(1, 64, 2, 8, 2, 3, 1, 7, 1, 2)          \
-  X(2, 64, 4, 4, 2, 3, 1, 7, 1, 2)          \
-  X(3, 64, 2, 8, 4, 3, 1, 7, 1, 1)          \
-  X(4, 64, 2, 8, 2, 3, 1, 7, 1, 1)          \
-  X(5, 64, 4, 4, 1, 4, 1, 13, 1, 1)         \
-  X(6, 64, 4, 4, 1, 8, 1, 13, 1, 1)         \
-  X(7, 64, 4, 4, 2, 4, 1, 13, 1, 1)         \
-  X(8, 64, 2, 8, 1, 3, 1, 4, 1, 2)          \
-  X(9, 64, 2, 8, 1, 3, 1, 7, 2, 2)          \
-  X(10, 64, 4, 4, 1, 4, 1, 13, 2, 1)        \
-  X(11, 16, 2, 8, 1, 3, 1, 7, 2, 2)         \
-  X(12, 32, 2, 8, 1, 3, 1, 7, 2, 2)         \
-  X(13, 128, 2, 8, 1, 3, 1, 7, 1, 2)        \
-  X(14, 128, 2, 8, 2, 3, 1, 7, 1, 1)        \
-  X(15, 128, 2, 8, 1, 3, 1, 7, 2, 1)        \
-  X(16, 128, 4, 4, 1, 4, 1, 13, 1, 1)       \
-  X(17, 256, 2, 8, 1, 3, 1, 7, 2, 1)        \
-  X(18, 64, 2, 8, 4, 3, 1, 7, 1, 2)         \
-  X(19, 64, 4, 4, 4, 3, 1, 7, 1, 2)         \
-  X(20, 64, 2, 8, 1, 4, 1, 7, 1, 2)         \
-  X(21, 64, 2, 8, 1, 4, 1, 7, 1, 1)         \
-  X(22, 64, 4, 4, 1, 4, 1, 7, 2, 1)         \
-  X(23, 64, 4, 4, 1, 4, 1, 7, 2, 2)         \
-  X(24, 64, 4, 4, 2, 4, 1, 7, 2, 1)         \
-  X(25, 128, 2, 8, 1, 4, 1, 7, 1, 1)        \
-  X(26, 64, 2, 8, 2, 2, 2, 7, 1, 2)         \
-  X(27, 64, 2, 8, 4, 1, 3, 4, 2, 1)         \
-  X(28, 64, 2, 8, 2, 1, 3, 4, 2, 2)         \
-  X(29, 128, 2, 8, 2, 2, 2, 4, 2, 1)        \
-  X(30, 64, 2, 8, 1, 4, 1, 4, 2, 1)         \
-  X(31, 64, 2, 8, 1, 4, 1, 4, 2, 2)         \
-  X(32, 64, 4, 4, 1, 4, 1, 4, 2, 1)         \
-  X(33, 128, 2, 8, 1, 4, 1, 4, 2, 1)
+  X(0, 64, 2, 8, 1, 3, 1, 7, 1, 2, 0)          \
+  X(1, 64, 2, 8, 2, 3, 1, 7, 1, 2, 0)          \
+  X(2, 64, 4, 4, 2, 3, 1, 7, 1, 2, 0)          \
+  X(3, 64, 2, 8, 4, 3, 1, 7, 1, 1, 0)          \
+  X(4, 64, 2, 8, 2, 3, 1, 7, 1, 1, 0)          \
+  X(5, 64, 4, 4, 1, 4, 1, 13, 1, 1, 0)         \
+  X(6, 64, 4, 4, 1, 8, 1, 13, 1, 1, 0)         \
+  X(7, 64, 4, 4, 2, 4, 1, 13, 1, 1, 0)         \
+  X(8, 64, 2, 8, 1, 3, 1, 4, 1, 2, 0)          \
+  X(9, 64, 2, 8, 1, 3, 1, 7, 2, 2, 0)          \
+  X(10, 64, 4, 4, 1, 4, 1, 13, 2, 1, 0)        \
+  X(11, 16, 2, 8, 1, 3, 1, 7, 2, 2, 0)         \
+  X(12, 32, 2, 8, 1, 3, 1, 7, 2, 2, 0)         \
+  X(13, 128, 2, 8, 1, 3, 1, 7, 1, 2, 0)        \
+  X(14, 128, 2, 8, 2, 3, 1, 7, 1, 1, 0)        \
+  X(15, 128, 2, 8, 1, 3, 1, 7, 2, 1, 0)        \
+  X(16, 128, 4, 4, 1, 4, 1, 13, 1, 1, 0)       \
+  X(17, 256, 2, 8, 1, 3, 1, 7, 2, 1, 0)        \
+  X(18, 64, 2, 8, 4, 3, 1, 7, 1, 2, 0)         \
+  X(19, 64, 4, 4, 4, 3, 1, 7, 1, 2, 0)         \
+  X(20, 64, 2, 8, 1, 4, 1, 7, 1, 2, 0)         \
+  X(21, 64, 2, 8, 1, 4, 1, 7, 1, 1, 0)         \
+  X(22, 64, 4, 4, 1, 4, 1, 7, 2, 1, 0)         \
+  X(23, 64, 4, 4, 1, 4, 1, 7, 2, 2, 0)         \
+  X(24, 64, 4, 4, 2, 4, 1, 7, 2, 1, 0)         \
+  X(25, 128, 2, 8, 1, 4, 1, 7, 1, 1, 0)        \
+  X(26, 64, 2, 8, 2, 2, 2, 7, 1, 2, 0)         \
+  X(27, 64, 2, 8, 4, 1, 3, 4, 2, 1, 0)         \
+  X(28, 64, 2, 8, 2, 1, 3, 4, 2, 2, 0)         \
+  X(29, 128, 2, 8, 2, 2, 2, 4, 2, 1, 0)        \
+  X(30, 64, 2, 8, 1, 4, 1, 4, 2, 1, 0)         \
+  X(31, 64, 2, 8, 1, 4, 1, 4, 2, 2, 0)         \
+  X(32, 64, 4, 4, 1, 4, 1, 4, 2, 1, 0)         \
+  X(33, 128, 2, 8, 1, 4, 1, 4, 2, 1, 0) \
+  X(34, 64, 2, 8, 1, 4, 1, 7, 1, 1, 4)  \
+  X(35, 64, 4, 4, 1, 4, 1, 4, 2, 1, 4)  \
+  X(36, 64, 2, 8, 1, 4, 1, 4, 2, 1, 4)
 
 struct RollVariant {
-  int hd, qh, qw, wh, wt, ns, nk, ng, nbuf;
+  int hd, qh, qw, wh, wt, ns, nk, ng, nbuf, occ;
 };
 
 constexpr RollVariant kRollVariants[] = {
-#define NA3D_ROLL_ENTRY(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF) \
-  {HD, QH, QW, WH, WT, NS, NK, NG, NBUF},
+#define NA3D_ROLL_ENTRY(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC) \
+  {HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC},
     NA3D_ROLL_VARIANTS(NA3D_ROLL_ENTRY)
 #undef NA3D_ROLL_ENTRY
 };

@@ -125,11 +125,12 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[Slot<HD>::KSTEPS], const uin
   }
 }
 
+// A slot admits a query plane with m = -inf and whatever its accumulators
+// hold from the plane it served before: the first real score of the new
+// plane always moves the reference max, and that rescale multiplies the
+// accumulators by 0 (units before it add only exact zero weights).
 template <int HD>
 __device__ __forceinline__ void reset_state(Slot<HD>& S) {
-#pragma unroll
-  for (int mt = 0; mt < Slot<HD>::MT; ++mt) S.acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  S.accl = f32x4{0.f, 0.f, 0.f, 0.f};
   S.m = kNegInf;
 }
 
@@ -205,8 +206,9 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
 }
 
-template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF>
-__global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const RollArgs a) {
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
+__global__ void __launch_bounds__(kWave * WH * WT) __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1)))
+na3d_fwd_roll_kernel(const RollArgs a) {
   static_assert(QH * QW == 16, "a wave owns 16 queries");
   static_assert(NBUF == 1 || NBUF == 2, "one or two plane buffers");
   constexpr int KSTEPS = Slot<HD>::KSTEPS;
@@ -424,6 +426,9 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
   for (int s = 0; s < NS; ++s) {
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) S[s].qf[ks] = bf16x8{};
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) S[s].acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    S[s].accl = f32x4{0.f, 0.f, 0.f, 0.f};
     reset_state(S[s]);
   }
   bf16x8 qn[KSTEPS];          // Q of query plane qn_t, fetched one key plane early
@@ -528,10 +533,12 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
         // exceeds it by more than kRescale
         auto unit_max = [&](int u, const f32x4 (&in)[NK]) __attribute__((always_inline)) {
           const int sl = u % NS;
-          float mx = kNegInf;
+          // a chain of three-input maxes: two new scores per instruction
+          float mx = __builtin_fmaxf(__builtin_fmaxf(in[0][0], in[0][1]), in[0][2]);
 #pragma unroll
-          for (int c = 0; c < NK; ++c)
-            mx = fmaxf(mx, fmaxf(fmaxf(in[c][0], in[c][1]), fmaxf(in[c][2], in[c][3])));
+          for (int i = 3; i + 1 < 4 * NK; i += 2)
+            mx = __builtin_fmaxf(__builtin_fmaxf(mx, in[i >> 2][i & 3]), in[(i + 1) >> 2][(i + 1) & 3]);
+          if ((4 * NK - 3) & 1) mx = __builtin_fmaxf(mx, in[NK - 1][3]);
           mx = xmax4(mx);
           if (__builtin_amdgcn_ballot_w64(mx > S[sl].m + kRescale && mx > kRealScore) != 0) {
             const float mn = mx > kRealScore ? fmaxf(S[sl].m, mx) : S[sl].m;
@@ -633,9 +640,9 @@ __global__ void __launch_bounds__(kWave * WH * WT) na3d_fwd_roll_kernel(const Ro
 }
 
 // ------------------------------------------------------------------ launch
-template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF>
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
 int launch_cfg(const RollArgs& a, const Launch& l, hipStream_t stream) {
-  auto kern = na3d_fwd_roll_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF>;
+  auto kern = na3d_fwd_roll_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>;
   if (l.lds_bytes > 64 * 1024 &&
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, l.lds_bytes) != hipSuccess)
@@ -662,8 +669,8 @@ int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s) {
   a.lds_rows = l.lds_rows;
   if (l.variant < 0 || l.variant >= kNumRollVariants || kRollVariants[l.variant].hd != hd) return -1;
   switch (l.variant) {
-#define NA3D_ROLL_CASE(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF) \
-  case i: return launch_cfg<HD, QH, QW, WH, WT, NS, NK, NG, NBUF>(a, l, s);
+#define NA3D_ROLL_CASE(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC) \
+  case i: return launch_cfg<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>(a, l, s);
     NA3D_ROLL_VARIANTS(NA3D_ROLL_CASE)
 #undef NA3D_ROLL_CASE
     default: return -1;

@@ -217,8 +217,8 @@ bool plan_roll(int v, int B, int T, int H, int W, int NH, int HD, int KT, int KH
 int pick_roll(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, Launch* l) {
   static const int p16[] = {11};
   static const int p32[] = {12};
-  static const int p64_small[] = {28, 8, 26, 21, 20, 9};   // union <= 64 keys
-  static const int p64_mid[] = {26, 21, 20, 1, 9, 10};     // union <= 112 keys
+  static const int p64_small[] = {8, 34, 21, 26, 20, 9};       // union <= 64 keys
+  static const int p64_mid[] = {35, 26, 34, 21, 20, 1, 9, 10};  // union <= 112 keys
   static const int p64_large[] = {5, 10, 22, 6, 7, 9};     // larger windows
   static const int p128[] = {25, 15, 14, 13, 16, 29};
   static const int p256[] = {17};
