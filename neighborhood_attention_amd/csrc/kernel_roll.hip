@@ -202,6 +202,26 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t ofs, uint32_t l
       : "memory");
 }
 
+// The same for a K row chunk and the V row chunk at the same source offset,
+// landing vgap bytes apart in LDS: one M0 save/restore for the pair.
+__device__ __forceinline__ void dma16_kv(const void* kbase, const void* vbase, uint32_t ofs, uint32_t lds,
+                                         uint32_t vgap) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_add_u32 m0, m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %3\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(ofs), "s"(kbase), "s"(vbase), "s"(lds), "s"(vgap)
+      : "memory", "scc");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
 }
@@ -385,26 +405,33 @@ na3d_fwd_roll_kernel(const RollArgs a) {
   const uint32_t dwrap = (uint32_t)(W - hwd) * tok_b;              // halo row carry
   const int rw0 = row0 % hwd;
   const uint32_t d0 = (uint32_t)((hh0 + row0 / hwd) * W + hw0 + rw0) * tok_b + (uint32_t)(n * HD * 2);
+  // When a round advances a multiple of 16 rows, a lane's swizzled chunk is
+  // the same in every round and is folded into its start offset.
+  constexpr bool kFixedSwz = RSTEP % 16 == 0;
+  const uint32_t d0s = d0 + (kFixedSwz ? (uint32_t)((pc ^ swz(HD, row0)) << 4) : 0u);
+  const int full_rounds = total_chunks / NT;  // rounds in which every lane has a chunk
   auto issue_stage = [&](int tp, int bufi) {
     const uint16_t* kpl = a.k + (int64_t)b * T * plane + (int64_t)tp * plane;
     const uint16_t* vpl = a.v + (int64_t)b * T * plane + (int64_t)tp * plane;
     const uint32_t dk = lds_addr(smem + bufi * 2 * buf_bytes + wave * kWave * 16);
-    const uint32_t dv = dk + buf_bytes;
-    uint32_t d = d0;
-    int rw = rw0;
-    for (int c0 = 0, row = row0; c0 < total_chunks; c0 += NT, row += RSTEP) {
-      if (c0 + tid < total_chunks) {
-        const uint32_t o = d + (uint32_t)((pc ^ swz(HD, row)) << 4);
-        dma16(kpl, o, dk + c0 * 16);
-        dma16(vpl, o, dv + c0 * 16);
-      }
+    uint32_t d = d0s;
+    int rw = rw0, row = row0;
+    auto advance = [&]() {
       d += dstep;
       rw += step_w;
+      row += RSTEP;
       if (rw >= hwd) {
         rw -= hwd;
         d += dwrap;
       }
+    };
+    auto lane_ofs = [&]() { return kFixedSwz ? d : d + (uint32_t)((pc ^ swz(HD, row)) << 4); };
+    int r = 0;
+    for (; r < full_rounds; ++r) {
+      dma16_kv(kpl, vpl, lane_ofs(), dk + r * NT * 16, buf_bytes);
+      advance();
     }
+    if (r * NT + tid < total_chunks) dma16_kv(kpl, vpl, lane_ofs(), dk + r * NT * 16, buf_bytes);
   };
 
   // zero the rows past the halo in every buffer (never staged; read only as
