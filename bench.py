@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-large-window", action="store_true",
                     help="headline run without the 11x11x11 companion measurement")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="headline run without the fused-QKV input companion measurement")
     ap.add_argument("--no-check", action="store_true",
                     help="skip the sampled parity check before timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -232,6 +234,45 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0):
     return rec
 
 
+def bench_fused(name, steps, warmup):
+    """The headline workload with q, k, v read in place from one fused
+    (B,T,H,W,3,NH,HD) QKV buffer through the strided entry point, against
+    first copying them out to contiguous tensors (what a launcher that only
+    takes contiguous inputs must do).  Returns kernel-time figures."""
+    import torch
+
+    import neighborhood_attention_amd as na
+    from na3d_inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(w.shape, w.seed, "cuda", w.k_outlier_frac)
+    qkv = torch.stack([q, k, v], dim=4).contiguous()
+    del q, k, v
+    qs, ks, vs = (qkv[:, :, :, :, i] for i in range(3))
+    out = torch.empty(w.shape, dtype=torch.bfloat16, device="cuda")
+    ref = na.fwd(qs.contiguous(), ks.contiguous(), vs.contiguous(), w.window)
+    na.fwd(qs, ks, vs, w.window, out=out)
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref):
+        raise SystemExit("fused-QKV output differs from the contiguous path")
+    _, strided_ms = time_kernel(lambda: na.fwd(qs, ks, vs, w.window, out=out), steps, warmup)
+    bufs = [torch.empty(w.shape, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+
+    def copy_then_run():
+        for dst, src in zip(bufs, (qs, ks, vs)):
+            dst.copy_(src)
+        na.fwd(bufs[0], bufs[1], bufs[2], w.window, out=out)
+
+    _, copy_ms = time_kernel(copy_then_run, steps, warmup)
+    return {
+        "layout": "(B,T,H,W,3,NH,HD) fused QKV buffer, q/k/v as strided views",
+        "value": round(w.flops / (strided_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "kernel_us_strided": round(strided_ms * 1e3, 2),
+        "us_copy_to_contiguous_then_kernel": round(copy_ms * 1e3, 2),
+        "bitwise_equal_to_contiguous": True,
+    }
+
+
 def copy_calibration(nbytes):
     """A plain device copy of a known size, for scaling memory counters."""
     import torch
@@ -276,6 +317,8 @@ def main():
             "value": lw["value"], "unit": "TFLOP/s", "mfma_peak_frac": lw["mfma_peak_frac"],
             "ms_per_step": lw["ms_per_step"], "kernel_us": lw["kernel_us"],
             "roofline": lw["roofline"], "parity_sampled": lw["parity_sampled"]}
+    if args.workload == HEADLINE and not args.no_fused:
+        rec["fused_qkv_inputs"] = bench_fused(args.workload, args.steps, args.warmup)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -51,6 +51,7 @@ extern "C" {
 #define NA3D_ERR_DEVICE (-7)   /* the current HIP device is not gfx950 */
 #define NA3D_ERR_LAUNCH (-8)   /* the kernel launch was rejected by HIP */
 #define NA3D_ERR_CONFIG (-9)   /* an explicit launch configuration cannot run the sizes */
+#define NA3D_ERR_STRIDE (-10)  /* a stride set na3d_fwd_strided cannot take (see there) */
 
 /*
  * Forward pass of 3-D neighborhood attention.
@@ -119,6 +120,46 @@ int na3d_fwd_config(const void* q, const void* k, const void* v, void* out,
 int na3d_plan_config(int B, int T, int H, int W, int NH, int HD, int KT,
                      int KH, int KW, int family, int variant, int tile_t,
                      int* plan);
+
+/*
+ * na3d_fwd on strided tensors, so that q, k and v can be read in place as
+ * views of a fused QKV projection output (the pages' launcher makes a
+ * contiguous copy of v before its kernel, and that copy is inside their
+ * measured time: same PR, Performance), or of a head-major buffer.
+ *   strides: 20 element (not byte) strides, four groups of five, in the
+ *            order q, k, v, out; each group gives the step between
+ *            neighbouring elements along B, T, H, W and NH.  The HD axis is
+ *            contiguous (stride 1) in every tensor.  Element (b,t,h,w,n,d)
+ *            of tensor X is at X + b*sB + t*sT + h*sH + w*sW + n*sN + d.
+ *            The array is read during the call only.
+ * Contract (checked before any device call; NA3D_ERR_STRIDE otherwise):
+ *   - every stride is >= 0 and a multiple of 8 (16-byte rows stay aligned);
+ *   - k and v have the same H, W and NH strides (one staging offset serves
+ *     both; their B and T strides may differ);
+ *   - no two elements of out share an address (its strides, ordered by
+ *     size, each step over the whole extent of the smaller ones).
+ *   out must not overlap the address range of q, k or v (NA3D_ERR_OVERLAP);
+ *   q, k and v may overlap each other freely (they are only read).
+ * Everything else (pointers, sizes, alignment, ownership, stream, errors)
+ * is as for na3d_fwd, which is this call with the contiguous strides
+ *   sN = HD, sW = NH*HD, sH = W*NH*HD, sT = H*W*NH*HD, sB = T*H*W*NH*HD.
+ */
+int na3d_fwd_strided(const void* q, const void* k, const void* v, void* out,
+                     int B, int T, int H, int W, int NH, int HD, int KT,
+                     int KH, int KW, const long long* strides, void* stream);
+
+/* The argument checks of na3d_fwd_strided alone, without touching a device. */
+int na3d_check_args_strided(const void* q, const void* k, const void* v,
+                            const void* out, int B, int T, int H, int W,
+                            int NH, int HD, int KT, int KH, int KW,
+                            const long long* strides);
+
+/* na3d_fwd_config on strided tensors (contract of na3d_fwd_strided). */
+int na3d_fwd_strided_config(const void* q, const void* k, const void* v,
+                            void* out, int B, int T, int H, int W, int NH,
+                            int HD, int KT, int KH, int KW,
+                            const long long* strides, int family, int variant,
+                            int tile_t, void* stream);
 
 /* Number of rolling-family instantiations compiled into the library. */
 int na3d_num_variants(void);

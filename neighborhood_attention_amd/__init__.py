@@ -30,9 +30,11 @@ NA3D_ERR_OVERLAP = -6
 NA3D_ERR_DEVICE = -7
 NA3D_ERR_LAUNCH = -8
 NA3D_ERR_CONFIG = -9
+NA3D_ERR_STRIDE = -10
 
 EXPORTS = ("na3d_fwd", "na3d_check_args", "na3d_status_string", "na3d_plan",
-           "na3d_fwd_config", "na3d_plan_config", "na3d_num_variants", "na3d_abi_version")
+           "na3d_fwd_config", "na3d_plan_config", "na3d_fwd_strided", "na3d_check_args_strided",
+           "na3d_fwd_strided_config", "na3d_num_variants", "na3d_abi_version")
 PLAN_KEYS = ("family", "tile_t", "tile_h", "tile_w", "workgroups", "threads", "lds_bytes",
              "planes", "variant", "runs")
 
@@ -69,6 +71,13 @@ def load(path: str = LIB_PATH):
         lib.na3d_fwd_config.restype = i32
         lib.na3d_plan_config.argtypes = [i32] * 12 + [ctypes.POINTER(i32)]
         lib.na3d_plan_config.restype = i32
+        ll = ctypes.POINTER(ctypes.c_longlong)
+        lib.na3d_fwd_strided.argtypes = [p, p, p, p] + [i32] * 9 + [ll, p]
+        lib.na3d_fwd_strided.restype = i32
+        lib.na3d_check_args_strided.argtypes = [p, p, p, p] + [i32] * 9 + [ll]
+        lib.na3d_check_args_strided.restype = i32
+        lib.na3d_fwd_strided_config.argtypes = [p, p, p, p] + [i32] * 9 + [ll] + [i32] * 3 + [p]
+        lib.na3d_fwd_strided_config.restype = i32
         lib.na3d_num_variants.argtypes = []
         lib.na3d_num_variants.restype = i32
         lib.na3d_abi_version.argtypes = []
@@ -89,6 +98,23 @@ def check_args(q_ptr, k_ptr, v_ptr, out_ptr, shape, kernel_size) -> int:
                                   KT, KH, KW)
 
 
+def _stride_array(strides):
+    """20 element strides (B, T, H, W, NH of q, k, v, out) as a C array."""
+    flat = [int(x) for group in strides for x in group]
+    if len(flat) != 20:
+        raise ValueError("expected 4 groups of 5 strides, got %d values" % len(flat))
+    return (ctypes.c_longlong * 20)(*flat)
+
+
+def check_args_strided(q_ptr, k_ptr, v_ptr, out_ptr, shape, kernel_size, strides) -> int:
+    """Host-only argument check of the strided entry point (no device access).
+    ``strides`` = four (sB, sT, sH, sW, sN) element-stride tuples: q, k, v, out."""
+    B, T, H, W, NH, HD = (int(x) for x in shape)
+    KT, KH, KW = (int(x) for x in kernel_size)
+    return load().na3d_check_args_strided(q_ptr, k_ptr, v_ptr, out_ptr, B, T, H, W, NH, HD,
+                                          KT, KH, KW, _stride_array(strides))
+
+
 def plan(shape, kernel_size, family: int = 0, variant: int = 0, tile_t: int = 0) -> dict:
     """Launch plan for these sizes (automatic, or an explicit configuration)."""
     B, T, H, W, NH, HD = (int(x) for x in shape)
@@ -106,12 +132,23 @@ def num_variants() -> int:
 
 
 def fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, shape, kernel_size,
-            stream: int = 0, config=None) -> None:
+            stream: int = 0, config=None, strides=None) -> None:
     """Call na3d_fwd (or na3d_fwd_config when ``config`` = (family, variant,
-    tile_t) is given) on raw device addresses; raises NA3DError on failure."""
+    tile_t) is given; the strided entry points when ``strides`` = four
+    (sB, sT, sH, sW, sN) element-stride tuples for q, k, v, out is given) on
+    raw device addresses; raises NA3DError on failure."""
     B, T, H, W, NH, HD = (int(x) for x in shape)
     KT, KH, KW = (int(x) for x in kernel_size)
-    if config is None:
+    if strides is not None:
+        st = _stride_array(strides)
+        if config is None:
+            rc = load().na3d_fwd_strided(q_ptr, k_ptr, v_ptr, out_ptr, B, T, H, W, NH, HD, KT,
+                                         KH, KW, st, stream)
+        else:
+            fam, var, tt = (int(x) for x in config)
+            rc = load().na3d_fwd_strided_config(q_ptr, k_ptr, v_ptr, out_ptr, B, T, H, W, NH,
+                                                HD, KT, KH, KW, st, fam, var, tt, stream)
+    elif config is None:
         rc = load().na3d_fwd(q_ptr, k_ptr, v_ptr, out_ptr, B, T, H, W, NH, HD, KT, KH, KW,
                              stream)
     else:
@@ -125,9 +162,12 @@ def fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, shape, kernel_size
 def fwd(q, k, v, kernel_size, out=None, config=None):
     """3-D neighborhood attention forward on (B,T,H,W,NH,HD) bf16 CUDA tensors.
 
-    Returns ``out`` (allocated with ``torch.empty_like(q)`` when not given).
-    The kernel is enqueued on torch's current stream.  ``config`` =
-    (family, variant, tile_t) forces a launch configuration (tuning/testing).
+    q, k, v (and out) may be strided views, e.g. slices of a fused QKV
+    projection output, as long as the HD axis is contiguous; they are then
+    read in place through na3d_fwd_strided.  Returns ``out`` (a new
+    contiguous tensor when not given).  The kernel is enqueued on torch's
+    current stream.  ``config`` = (family, variant, tile_t) forces a launch
+    configuration (tuning/testing).
     """
     import torch
 
@@ -138,8 +178,8 @@ def fwd(q, k, v, kernel_size, out=None, config=None):
             raise TypeError("%s must be bfloat16, got %s" % (name, t.dtype))
         if t.device.type != "cuda":
             raise ValueError("%s must be a GPU tensor" % name)
-        if not t.is_contiguous():
-            raise ValueError("%s must be contiguous" % name)
+        if t.dim() == 6 and t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError("%s must have a contiguous last (head-dim) axis" % name)
     if q.dim() != 6:
         raise ValueError("expected (B,T,H,W,NH,HD) tensors, got %d dims" % q.dim())
     if not (q.shape == k.shape == v.shape):
@@ -147,12 +187,16 @@ def fwd(q, k, v, kernel_size, out=None, config=None):
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v are on different devices")
     if out is None:
-        out = torch.empty_like(q)
-    elif (out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous()
-          or out.device != q.device):
-        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    elif (out.shape != q.shape or out.dtype != torch.bfloat16 or out.device != q.device
+          or (out.shape[-1] > 1 and out.stride(-1) != 1)):
+        raise ValueError("out must be a bf16 tensor shaped like q with a contiguous last axis")
+    tensors = (q, k, v, out)
+    strides = None
+    if not all(t.is_contiguous() for t in tensors):
+        strides = [tuple(int(x) for x in t.stride()[:5]) for t in tensors]
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), q.shape,
-                kernel_size, stream, config)
+                kernel_size, stream, config, strides)
     return out

@@ -65,6 +65,12 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
   return (i & 7) * per + (i >> 3);
 }
 
+// Element strides of one (B,T,H,W,NH,HD) tensor along B, T, H, W and NH
+// (HD is contiguous).
+struct Strides {
+  int64_t b, t, h, w, n;
+};
+
 struct Problem {
   const uint16_t* q;
   const uint16_t* k;
@@ -72,6 +78,7 @@ struct Problem {
   uint16_t* o;
   int B, T, H, W, NH;
   int KT, KH, KW;
+  Strides sq, sk, sv, so;  // k and v share h, w and n
 };
 
 // Launch description chosen by the host planner.

@@ -40,6 +40,7 @@ struct GeneralArgs {
   int KT, KH, KW;
   int tiles_h, tiles_w;
   int lds_rows;  // capacity of each of the K and V staging buffers, in rows
+  Strides sq, sk, sv, so;  // element strides; k and v share h, w and n
 };
 
 __device__ __forceinline__ void divmod(int u, int d, int& qo, int& ro) {
@@ -124,15 +125,12 @@ na3d_fwd_general_kernel(const GeneralArgs a) {
   const int uw = wave_active ? win_start(bw1, KW, W) + KW - uw0 : 1;
   const int oh = uh0 - hh0, ow = uw0 - hw0;  // union origin inside the halo
 
-  const int64_t tok_stride = (int64_t)a.NH * HD;
-  const int64_t plane_stride = (int64_t)H * W * tok_stride;
-  const int64_t batch_base = (int64_t)b * a.T * plane_stride + (int64_t)n * HD;
 
   // ---- Q^T operand (B of S^T = K.Q^T): lane (q16, g) holds hd [32ks+8g, +8)
   bf16x8 qf[KSTEPS];
   {
-    const uint16_t* qp = a.q + batch_base + (int64_t)t * plane_stride +
-                         ((int64_t)qhc * W + qwc) * tok_stride;
+    const uint16_t* qp = a.q + (int64_t)b * a.sq.b + (int64_t)t * a.sq.t + (int64_t)n * a.sq.n +
+                         (int64_t)qhc * a.sq.h + (int64_t)qwc * a.sq.w;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const int d = 32 * ks + 8 * g;
@@ -152,8 +150,8 @@ na3d_fwd_general_kernel(const GeneralArgs a) {
   const int nchunk = (halo_rows + a.lds_rows - 1) / a.lds_rows;
   for (int dt = 0; dt < a.KT; ++dt) {
     const int tp = st + dt;
-    const uint16_t* kplane = a.k + batch_base + (int64_t)tp * plane_stride;
-    const uint16_t* vplane = a.v + batch_base + (int64_t)tp * plane_stride;
+    const uint16_t* kplane = a.k + (int64_t)b * a.sk.b + (int64_t)tp * a.sk.t + (int64_t)n * a.sk.n;
+    const uint16_t* vplane = a.v + (int64_t)b * a.sv.b + (int64_t)tp * a.sv.t + (int64_t)n * a.sk.n;
     for (int c = 0; c < nchunk; ++c) {
       const int r0 = c * a.lds_rows;
       const int r1 = min(r0 + a.lds_rows, halo_rows);
@@ -164,7 +162,7 @@ na3d_fwd_general_kernel(const GeneralArgs a) {
         const int row = i / PARTS, part = i % PARTS;
         const int fr = r0 + row;
         const int hp = hh0 + fr / hwd, wp = hw0 + fr % hwd;
-        const int64_t off = ((int64_t)hp * W + wp) * tok_stride + part * 8;
+        const int64_t off = (int64_t)hp * a.sk.h + (int64_t)wp * a.sk.w + part * 8;
         const uint4 kv = *reinterpret_cast<const uint4*>(kplane + off);
         const uint4 vv = *reinterpret_cast<const uint4*>(vplane + off);
         *reinterpret_cast<uint4*>(lds_k + row * ROW + part * 16) = kv;
@@ -268,8 +266,8 @@ na3d_fwd_general_kernel(const GeneralArgs a) {
   l_run += __shfl_xor(l_run, 32);
   if (qvalid) {
     const float inv = 1.f / l_run;
-    uint16_t* op = a.o + batch_base + (int64_t)t * plane_stride +
-                   ((int64_t)qh * W + qw) * tok_stride;
+    uint16_t* op = a.o + (int64_t)b * a.so.b + (int64_t)t * a.so.t + (int64_t)n * a.so.n +
+                   (int64_t)qh * a.so.h + (int64_t)qw * a.so.w;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[mt][0] * inv) |
@@ -310,6 +308,10 @@ int launch_general(const Problem& p, const Launch& l, int hd, hipStream_t s) {
   a.tiles_h = l.tiles_h;
   a.tiles_w = l.tiles_w;
   a.lds_rows = l.lds_rows;
+  a.sq = p.sq;
+  a.sk = p.sk;
+  a.sv = p.sv;
+  a.so = p.so;
   switch (hd) {
     case 16: return launch_hd<16>(a, l, s);
     case 32: return launch_hd<32>(a, l, s);

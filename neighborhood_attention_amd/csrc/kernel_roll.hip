@@ -81,6 +81,7 @@ struct RollArgs {
   int nruns;     // runs along T
   int rpw;       // consecutive runs streamed by one workgroup
   int lds_rows;  // rows of each K and V staging buffer
+  Strides sq, sk, sv, so;  // element strides; k and v share h, w and n
 };
 
 // Max over the 4 lanes (l, l^16, l^32, l^48) that hold one query,
@@ -388,10 +389,11 @@ na3d_fwd_roll_kernel(const RollArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) vofs[mt] = v_addr<HD>(rb + vp, mt, q16);
 
-  const int64_t tok = (int64_t)a.NH * HD;
-  const int64_t plane = (int64_t)H * W * tok;
-  const int64_t bbase = (int64_t)b * T * plane + (int64_t)n * HD;
-  const int64_t qtok = ((int64_t)qhc * W + qwc) * tok;
+  // this lane's query token in (b, n) of q and out; plane t adds t * sT
+  const uint16_t* const qbase = a.q + (int64_t)b * a.sq.b + (int64_t)n * a.sq.n +
+                                (int64_t)qhc * a.sq.h + (int64_t)qwc * a.sq.w;
+  uint16_t* const obase = a.o + (int64_t)b * a.so.b + (int64_t)n * a.so.n +
+                          (int64_t)qhc * a.so.h + (int64_t)qwc * a.so.w;
 
   // ---- DMA staging walk: round k moves chunks [k*NT, (k+1)*NT); lane P of a
   // wave lands at chunk P of the buffer (row P / CPR, physical chunk P % CPR).
@@ -400,19 +402,23 @@ na3d_fwd_roll_kernel(const RollArgs a) {
   const int pc = tid % CPR;
   const int row0 = tid / CPR;
   const int step_h = RSTEP / hwd, step_w = RSTEP % hwd;
-  const uint32_t tok_b = (uint32_t)(a.NH * HD * 2);               // bytes per token
-  const uint32_t dstep = (uint32_t)(step_h * W + step_w) * tok_b;  // one round
-  const uint32_t dwrap = (uint32_t)(W - hwd) * tok_b;              // halo row carry
+  // byte steps of K/V along W and H (32-bit: the host keeps one head's
+  // spatial plane below 4 GiB for this family; wrapping arithmetic is exact)
+  const uint32_t sw_b = (uint32_t)(a.sk.w * 2), sh_b = (uint32_t)(a.sk.h * 2);
+  const uint32_t dstep = (uint32_t)step_h * sh_b + (uint32_t)step_w * sw_b;  // one round
+  const uint32_t dwrap = sh_b - (uint32_t)hwd * sw_b;                       // halo row carry
   const int rw0 = row0 % hwd;
-  const uint32_t d0 = (uint32_t)((hh0 + row0 / hwd) * W + hw0 + rw0) * tok_b + (uint32_t)(n * HD * 2);
+  const uint32_t d0 = (uint32_t)(hh0 + row0 / hwd) * sh_b + (uint32_t)(hw0 + rw0) * sw_b;
+  const uint16_t* const kbase = a.k + (int64_t)b * a.sk.b + (int64_t)n * a.sk.n;
+  const uint16_t* const vbase = a.v + (int64_t)b * a.sv.b + (int64_t)n * a.sk.n;
   // When a round advances a multiple of 16 rows, a lane's swizzled chunk is
   // the same in every round and is folded into its start offset.
   constexpr bool kFixedSwz = RSTEP % 16 == 0;
   const uint32_t d0s = d0 + (kFixedSwz ? (uint32_t)((pc ^ swz(HD, row0)) << 4) : 0u);
   const int full_rounds = total_chunks / NT;  // rounds in which every lane has a chunk
   auto issue_stage = [&](int tp, int bufi) {
-    const uint16_t* kpl = a.k + (int64_t)b * T * plane + (int64_t)tp * plane;
-    const uint16_t* vpl = a.v + (int64_t)b * T * plane + (int64_t)tp * plane;
+    const uint16_t* kpl = kbase + (int64_t)tp * a.sk.t;
+    const uint16_t* vpl = vbase + (int64_t)tp * a.sv.t;
     const uint32_t dk = lds_addr(smem + bufi * 2 * buf_bytes + wave * kWave * 16);
     uint32_t d = d0s;
     int rw = rw0, row = row0;
@@ -489,7 +495,7 @@ na3d_fwd_roll_kernel(const RollArgs a) {
 #pragma unroll
               for (int ks = 0; ks < KSTEPS; ++ks) S[s].qf[ks] = qn[ks];
             } else {
-              load_q<HD>(S[s].qf, a.q + bbase + (int64_t)tq(jhi) * plane + qtok, g);
+              load_q<HD>(S[s].qf, qbase + (int64_t)tq(jhi) * a.sq.t, g);
             }
             reset_state(S[s]);
           }
@@ -514,7 +520,7 @@ na3d_fwd_roll_kernel(const RollArgs a) {
           tn = nt0 + it;
         }
         if (tn >= 0) {
-          load_q<HD>(qn, a.q + bbase + (int64_t)tn * plane + qtok, g);
+          load_q<HD>(qn, qbase + (int64_t)tn * a.sq.t, g);
           qn_t = tn;
         }
       }
@@ -651,7 +657,7 @@ na3d_fwd_roll_kernel(const RollArgs a) {
 #pragma unroll
           for (int s = 0; s < NS; ++s)
             if (s == sl) pack_out<HD>(S[s], pend);
-          pend_p = a.o + bbase + (int64_t)tq(jlo) * plane + qtok;
+          pend_p = obase + (int64_t)tq(jlo) * a.so.t;
           pend_on = true;
         }
         ++jlo;
@@ -694,6 +700,10 @@ int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s) {
   a.nruns = l.nruns;
   a.rpw = l.rpw;
   a.lds_rows = l.lds_rows;
+  a.sq = p.sq;
+  a.sk = p.sk;
+  a.sv = p.sv;
+  a.so = p.so;
   if (l.variant < 0 || l.variant >= kNumRollVariants || kRollVariants[l.variant].hd != hd) return -1;
   switch (l.variant) {
 #define NA3D_ROLL_CASE(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC) \

@@ -26,9 +26,10 @@ constexpr int kTargetWorkgroups = 1024;      // 256 CUs x 4
 
 bool head_dim_ok(int hd) { return hd == 16 || hd == 32 || hd == 64 || hd == 128 || hd == 256; }
 
-bool overlaps(const void* a, const void* b, size_t bytes) {
+// Do the byte ranges [a, a + na) and [b, b + nb) intersect?
+bool overlaps2(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + bytes && y < x + bytes;
+  return x < y + nb && y < x + na;
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -40,6 +41,61 @@ int check_sizes(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int 
   if ((int64_t)T * H * W > ((int64_t)1 << 30)) return NA3D_ERR_SHAPE;
   if ((int64_t)B * T * H * W * NH * HD > ((int64_t)1 << 61)) return NA3D_ERR_SHAPE;
   if (KT < 1 || KH < 1 || KW < 1 || KT > T || KH > H || KW > W) return NA3D_ERR_WINDOW;
+  return NA3D_OK;
+}
+
+Strides contiguous(int T, int H, int W, int NH, int HD) {
+  Strides s;
+  s.n = HD;
+  s.w = (int64_t)NH * HD;
+  s.h = (int64_t)W * s.w;
+  s.t = (int64_t)H * s.h;
+  s.b = (int64_t)T * s.t;
+  return s;
+}
+
+// Element offset of the last element of a tensor, plus one.
+int64_t extent(const Strides& s, int B, int T, int H, int W, int NH, int HD) {
+  return (int64_t)(B - 1) * s.b + (int64_t)(T - 1) * s.t + (int64_t)(H - 1) * s.h +
+         (int64_t)(W - 1) * s.w + (int64_t)(NH - 1) * s.n + HD;
+}
+
+// Bytes spanned by the spatial (H, W) part of one K/V plane of one head: the
+// rolling family stages it with 32-bit byte offsets.
+int64_t kv_span_bytes(const Strides& sk, int H, int W, int HD) {
+  return 2 * ((int64_t)(H - 1) * sk.h + (int64_t)(W - 1) * sk.w + HD);
+}
+
+// Stride contract of the strided entry points; st = {q, k, v, out}.
+int check_strides(const void* q, const void* k, const void* v, const void* out, int B, int T,
+                  int H, int W, int NH, int HD, const Strides* st) {
+  const int64_t lim = (int64_t)1 << 56;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t x[5] = {st[i].b, st[i].t, st[i].h, st[i].w, st[i].n};
+    for (int j = 0; j < 5; ++j)
+      if (x[j] < 0 || x[j] % 8 != 0 || x[j] > lim) return NA3D_ERR_STRIDE;
+  }
+  if (st[1].h != st[2].h || st[1].w != st[2].w || st[1].n != st[2].n) return NA3D_ERR_STRIDE;
+  // no two elements of out at one address: ordered by stride, every axis of
+  // extent > 1 steps over the whole span of the smaller ones (HD first)
+  {
+    int64_t ext[5] = {B, T, H, W, NH};
+    int64_t str[5] = {st[3].b, st[3].t, st[3].h, st[3].w, st[3].n};
+    int idx[5] = {0, 1, 2, 3, 4};
+    std::sort(idx, idx + 5, [&](int a, int b) { return str[a] < str[b]; });
+    int64_t span = HD;
+    for (int j = 0; j < 5; ++j) {
+      const int a = idx[j];
+      if (ext[a] == 1) continue;
+      if (str[a] < span) return NA3D_ERR_STRIDE;
+      span = str[a] * (ext[a] - 1) + span;
+    }
+  }
+  const size_t bo = 2 * (size_t)extent(st[3], B, T, H, W, NH, HD);
+  if (overlaps2(out, bo, q, 2 * (size_t)extent(st[0], B, T, H, W, NH, HD)) ||
+      overlaps2(out, bo, k, 2 * (size_t)extent(st[1], B, T, H, W, NH, HD)) ||
+      overlaps2(out, bo, v, 2 * (size_t)extent(st[2], B, T, H, W, NH, HD)))
+    return NA3D_ERR_OVERLAP;
   return NA3D_OK;
 }
 
@@ -153,12 +209,12 @@ bool plan_general(int B, int T, int H, int W, int NH, int HD, int KT, int KH, in
 
 // Can rolling variant v run these sizes?  tile_t = 0 picks the run length.
 bool plan_roll(int v, int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
-               int tile_t, Launch* l) {
+               int tile_t, int64_t kv_span, Launch* l) {
   if (v < 0 || v >= kNumRollVariants) return false;
   const RollVariant& rv = kRollVariants[v];
   if (rv.hd != HD) return false;
-  // staging offsets are 32-bit byte offsets within one K/V plane
-  if ((int64_t)H * W * NH * HD * 2 >= ((int64_t)1 << 32)) return false;
+  // staging offsets are 32-bit byte offsets within one head's K/V plane
+  if (kv_span >= ((int64_t)1 << 32)) return false;
   const int BH = rv.wh * rv.qh;
   const int hwd_max = std::min(rv.qw + KW - 1, W);
   const int un_max = std::min(rv.qh + KH - 1, H) * hwd_max;
@@ -214,7 +270,8 @@ bool plan_roll(int v, int B, int T, int H, int W, int NH, int HD, int KT, int KH
 // Preferred rolling instantiations, best first (from measured sweeps), by
 // head dimension and by the union of one 2x8 query block's windows; the first
 // whose static limits fit the sizes wins.
-int pick_roll(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, Launch* l) {
+int pick_roll(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, int64_t kv_span,
+              Launch* l) {
   static const int p16[] = {11};
   static const int p32[] = {12};
   static const int p64_small[] = {8, 34, 21, 26, 20, 9};       // union <= 64 keys
@@ -241,24 +298,25 @@ int pick_roll(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW
     default: pref = p256; np = 1; break;
   }
   for (int i = 0; i < np; ++i)
-    if (plan_roll(pref[i], B, T, H, W, NH, HD, KT, KH, KW, 0, l)) return 1;
+    if (plan_roll(pref[i], B, T, H, W, NH, HD, KT, KH, KW, 0, kv_span, l)) return 1;
   return 0;
 }
 
-int make_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, Launch* l) {
-  if (pick_roll(B, T, H, W, NH, HD, KT, KH, KW, l)) return NA3D_OK;
+int make_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, int64_t kv_span,
+              Launch* l) {
+  if (pick_roll(B, T, H, W, NH, HD, KT, KH, KW, kv_span, l)) return NA3D_OK;
   if (plan_general(B, T, H, W, NH, HD, KT, KH, KW, l)) return NA3D_OK;
   return NA3D_ERR_SHAPE;
 }
 
 int make_plan_config(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
-                     int family, int variant, int tile_t, Launch* l) {
-  if (family == 0) return make_plan(B, T, H, W, NH, HD, KT, KH, KW, l);
+                     int family, int variant, int tile_t, int64_t kv_span, Launch* l) {
+  if (family == 0) return make_plan(B, T, H, W, NH, HD, KT, KH, KW, kv_span, l);
   if (family == 1)
     return plan_general(B, T, H, W, NH, HD, KT, KH, KW, l) ? NA3D_OK : NA3D_ERR_SHAPE;
   if (family == 2)
-    return plan_roll(variant, B, T, H, W, NH, HD, KT, KH, KW, tile_t, l) ? NA3D_OK
-                                                                          : NA3D_ERR_CONFIG;
+    return plan_roll(variant, B, T, H, W, NH, HD, KT, KH, KW, tile_t, kv_span, l) ? NA3D_OK
+                                                                                   : NA3D_ERR_CONFIG;
   return NA3D_ERR_CONFIG;
 }
 
@@ -293,7 +351,7 @@ int device_ok() {
 }
 
 int run(const void* q, const void* k, const void* v, void* out, int B, int T, int H, int W,
-        int NH, int HD, int KT, int KH, int KW, const Launch& l, void* stream) {
+        int NH, int HD, int KT, int KH, int KW, const Strides* st, const Launch& l, void* stream) {
   int rc = device_ok();
   if (rc != NA3D_OK) return rc;
   Problem p;
@@ -303,6 +361,7 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int T, in
   p.o = static_cast<uint16_t*>(out);
   p.B = B; p.T = T; p.H = H; p.W = W; p.NH = NH;
   p.KT = KT; p.KH = KH; p.KW = KW;
+  p.sq = st[0]; p.sk = st[1]; p.sv = st[2]; p.so = st[3];
   hipStream_t s = static_cast<hipStream_t>(stream);
   rc = l.family == 2 ? launch_roll(p, l, HD, s) : launch_general(p, l, HD, s);
   return rc == 0 ? NA3D_OK : NA3D_ERR_LAUNCH;
@@ -315,7 +374,7 @@ using namespace na3d;
 
 extern "C" {
 
-int na3d_abi_version(void) { return 2; }
+int na3d_abi_version(void) { return 3; }
 
 int na3d_num_variants(void) { return kNumRollVariants; }
 
@@ -331,8 +390,25 @@ const char* na3d_status_string(int status) {
     case NA3D_ERR_DEVICE: return "the current HIP device is not gfx950";
     case NA3D_ERR_LAUNCH: return "the kernel launch failed";
     case NA3D_ERR_CONFIG: return "the requested launch configuration cannot run these sizes";
+    case NA3D_ERR_STRIDE:
+      return "a stride is negative or not a multiple of 8, k and v differ in H/W/NH strides, "
+             "or out's strides map two elements to one address";
     default: return "unknown status";
   }
+}
+
+int na3d_check_args_strided(const void* q, const void* k, const void* v, const void* out, int B,
+                            int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
+                            const long long* strides) {
+  if (!q || !k || !v || !out || !strides) return NA3D_ERR_NULL;
+  const int rc = check_sizes(B, T, H, W, NH, HD, KT, KH, KW);
+  if (rc != NA3D_OK) return rc;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return NA3D_ERR_ALIGN;
+  Strides st[4];
+  for (int i = 0; i < 4; ++i)
+    st[i] = Strides{strides[5 * i], strides[5 * i + 1], strides[5 * i + 2], strides[5 * i + 3],
+                    strides[5 * i + 4]};
+  return check_strides(q, k, v, out, B, T, H, W, NH, HD, st);
 }
 
 int na3d_check_args(const void* q, const void* k, const void* v, const void* out, int B,
@@ -341,10 +417,9 @@ int na3d_check_args(const void* q, const void* k, const void* v, const void* out
   const int rc = check_sizes(B, T, H, W, NH, HD, KT, KH, KW);
   if (rc != NA3D_OK) return rc;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return NA3D_ERR_ALIGN;
-  const size_t bytes = (size_t)B * T * H * W * NH * HD * 2;
-  if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
-    return NA3D_ERR_OVERLAP;
-  return NA3D_OK;
+  const Strides c = contiguous(T, H, W, NH, HD);
+  const Strides st[4] = {c, c, c, c};
+  return check_strides(q, k, v, out, B, T, H, W, NH, HD, st);
 }
 
 int na3d_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, int* plan) {
@@ -357,7 +432,8 @@ int na3d_plan_config(int B, int T, int H, int W, int NH, int HD, int KT, int KH,
   int rc = check_sizes(B, T, H, W, NH, HD, KT, KH, KW);
   if (rc != NA3D_OK) return rc;
   Launch l;
-  rc = make_plan_config(B, T, H, W, NH, HD, KT, KH, KW, family, variant, tile_t, &l);
+  const int64_t span = kv_span_bytes(contiguous(T, H, W, NH, HD), H, W, HD);
+  rc = make_plan_config(B, T, H, W, NH, HD, KT, KH, KW, family, variant, tile_t, span, &l);
   if (rc != NA3D_OK) return rc;
   fill_plan(l, plan);
   return NA3D_OK;
@@ -371,12 +447,35 @@ int na3d_fwd(const void* q, const void* k, const void* v, void* out, int B, int 
 int na3d_fwd_config(const void* q, const void* k, const void* v, void* out, int B, int T,
                     int H, int W, int NH, int HD, int KT, int KH, int KW, int family,
                     int variant, int tile_t, void* stream) {
-  int rc = na3d_check_args(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW);
+  const Strides c = contiguous(T, H, W, NH, HD);
+  const long long st[20] = {c.b, c.t, c.h, c.w, c.n, c.b, c.t, c.h, c.w, c.n,
+                            c.b, c.t, c.h, c.w, c.n, c.b, c.t, c.h, c.w, c.n};
+  return na3d_fwd_strided_config(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW, st, family,
+                                 variant, tile_t, stream);
+}
+
+int na3d_fwd_strided(const void* q, const void* k, const void* v, void* out, int B, int T,
+                     int H, int W, int NH, int HD, int KT, int KH, int KW,
+                     const long long* strides, void* stream) {
+  return na3d_fwd_strided_config(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW, strides, 0, 0,
+                                 0, stream);
+}
+
+int na3d_fwd_strided_config(const void* q, const void* k, const void* v, void* out, int B,
+                            int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
+                            const long long* strides, int family, int variant, int tile_t,
+                            void* stream) {
+  int rc = na3d_check_args_strided(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW, strides);
   if (rc != NA3D_OK) return rc;
+  Strides st[4];
+  for (int i = 0; i < 4; ++i)
+    st[i] = Strides{strides[5 * i], strides[5 * i + 1], strides[5 * i + 2], strides[5 * i + 3],
+                    strides[5 * i + 4]};
   Launch l;
-  rc = make_plan_config(B, T, H, W, NH, HD, KT, KH, KW, family, variant, tile_t, &l);
+  rc = make_plan_config(B, T, H, W, NH, HD, KT, KH, KW, family, variant, tile_t,
+                        kv_span_bytes(st[1], H, W, HD), &l);
   if (rc != NA3D_OK) return rc;
-  return run(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW, l, stream);
+  return run(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW, st, l, stream);
 }
 
 }  // extern "C"

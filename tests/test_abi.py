@@ -39,7 +39,7 @@ def test_python_binding_lists_all_exports():
 
 
 def test_abi_version():
-    assert na.load().na3d_abi_version() == 2
+    assert na.load().na3d_abi_version() == 3
 
 
 def check(ptrs=(A, B_, C, O), shape=SHAPE, ks=KS):
@@ -102,7 +102,7 @@ def test_oversized_grid():
 
 
 def test_status_strings():
-    for code in range(0, -9, -1):
+    for code in range(0, -11, -1):
         s = na.status_string(code)
         assert s and s != "unknown status"
     assert na.status_string(-99) == "unknown status"
