@@ -56,6 +56,8 @@ def parse():
                     help="headline run without the 11x11x11 companion measurement")
     ap.add_argument("--no-fused", action="store_true",
                     help="headline run without the fused-QKV input companion measurement")
+    ap.add_argument("--no-split", action="store_true",
+                    help="headline run without the 2x2 query-box split companion measurement")
     ap.add_argument("--no-check", action="store_true",
                     help="skip the sampled parity check before timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -273,6 +275,46 @@ def bench_fused(name, steps, warmup):
     }
 
 
+def bench_split(name, steps, warmup):
+    """The headline workload's queries split into 2 x 2 boxes along H and W,
+    each computed by the query-box entry point with windows in the whole grid
+    (what one GPU of a spatial split runs), against one whole-grid launch."""
+    import torch
+
+    import neighborhood_attention_amd as na
+    from na3d_inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[name]
+    B, T, H, W, NH, HD = w.shape
+    q, k, v = make_inputs(w.shape, w.seed, "cuda", w.k_outlier_frac)
+    whole = torch.empty_like(q)
+    parts = torch.empty_like(q)
+    boxes = [(0, h0, w0, T, hq, wq) for h0, hq in ((0, H // 2), (H // 2, H - H // 2))
+             for w0, wq in ((0, W // 2), (W // 2, W - W // 2))]
+    views = [(q[:, :, b[1]:b[1] + b[4], b[2]:b[2] + b[5]],
+              parts[:, :, b[1]:b[1] + b[4], b[2]:b[2] + b[5]], b) for b in boxes]
+
+    def run_parts():
+        for qb, ob, b in views:
+            na.fwd_subgrid(qb, k, v, w.window, b[:3], out=ob)
+
+    na.fwd(q, k, v, w.window, out=whole)
+    run_parts()
+    torch.cuda.synchronize()
+    a = whole.double()
+    rel = float((parts.double() - a).norm() / a.norm())
+    if rel > 2e-3:
+        raise SystemExit("query-box split differs from the whole grid: rel %.3e" % rel)
+    _, whole_ms = time_kernel(lambda: na.fwd(q, k, v, w.window, out=whole), steps, warmup)
+    _, parts_ms = time_kernel(run_parts, steps, warmup)
+    return {
+        "boxes": [list(b) for b in boxes],
+        "kernel_us_whole": round(whole_ms * 1e3, 2),
+        "kernel_us_four_boxes": round(parts_ms * 1e3, 2),
+        "rel_l2_vs_whole": rel,
+    }
+
+
 def copy_calibration(nbytes):
     """A plain device copy of a known size, for scaling memory counters."""
     import torch
@@ -319,6 +361,8 @@ def main():
             "roofline": lw["roofline"], "parity_sampled": lw["parity_sampled"]}
     if args.workload == HEADLINE and not args.no_fused:
         rec["fused_qkv_inputs"] = bench_fused(args.workload, args.steps, args.warmup)
+    if args.workload == HEADLINE and not args.no_split:
+        rec["query_box_split_2x2"] = bench_split(args.workload, args.steps, args.warmup)
     print(json.dumps(rec), flush=True)
     return 0
 

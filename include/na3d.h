@@ -52,6 +52,7 @@ extern "C" {
 #define NA3D_ERR_LAUNCH (-8)   /* the kernel launch was rejected by HIP */
 #define NA3D_ERR_CONFIG (-9)   /* an explicit launch configuration cannot run the sizes */
 #define NA3D_ERR_STRIDE (-10)  /* a stride set na3d_fwd_strided cannot take (see there) */
+#define NA3D_ERR_BOX (-11)     /* a query box that is empty or reaches outside the grid */
 
 /*
  * Forward pass of 3-D neighborhood attention.
@@ -158,6 +159,42 @@ int na3d_check_args_strided(const void* q, const void* k, const void* v,
 int na3d_fwd_strided_config(const void* q, const void* k, const void* v,
                             void* out, int B, int T, int H, int W, int NH,
                             int HD, int KT, int KH, int KW,
+                            const long long* strides, int family, int variant,
+                            int tile_t, void* stream);
+
+/*
+ * Forward pass for the queries of a sub-box of the grid, with every window
+ * placed in the whole grid: the pages' exact reference takes a W sub-slice of
+ * q with the full k and v and global W coordinates for the window bounds
+ * (aiter PR, Technical Details); this is the same in all three axes, and is what a
+ * caller that splits one grid's queries (across launches or GPUs) needs.
+ *   k, v    : the whole grid, (B, T, H, W, NH, HD)
+ *   q, out  : the queries [t0, t0+Tq) x [h0, h0+Hq) x [w0, w0+Wq),
+ *             (B, Tq, Hq, Wq, NH, HD); element (b, i, j, l, n, d) is the
+ *             query at grid position (t0+i, h0+j, w0+l)
+ *   box     : 6 ints {t0, h0, w0, Tq, Hq, Wq}; 0 <= t0, t0 + Tq <= T, Tq >= 1
+ *             and likewise for H and W (NA3D_ERR_BOX otherwise)
+ *   strides : as for na3d_fwd_strided (q and out with the box extents), or
+ *             NULL for contiguous tensors of those shapes
+ * out[b, i, j, l, n, :] equals what na3d_fwd writes at (b, t0+i, h0+j, w0+l,
+ * n, :) for the whole grid.  Other arguments and the contract are those of
+ * na3d_fwd_strided.
+ */
+int na3d_fwd_subgrid(const void* q, const void* k, const void* v, void* out,
+                     int B, int T, int H, int W, int NH, int HD, int KT,
+                     int KH, int KW, const int* box, const long long* strides,
+                     void* stream);
+
+/* The argument checks of na3d_fwd_subgrid alone, without touching a device. */
+int na3d_check_args_subgrid(const void* q, const void* k, const void* v,
+                            const void* out, int B, int T, int H, int W,
+                            int NH, int HD, int KT, int KH, int KW,
+                            const int* box, const long long* strides);
+
+/* na3d_fwd_config for a query box (contract of na3d_fwd_subgrid). */
+int na3d_fwd_subgrid_config(const void* q, const void* k, const void* v,
+                            void* out, int B, int T, int H, int W, int NH,
+                            int HD, int KT, int KH, int KW, const int* box,
                             const long long* strides, int family, int variant,
                             int tile_t, void* stream);
 

@@ -31,10 +31,12 @@ NA3D_ERR_DEVICE = -7
 NA3D_ERR_LAUNCH = -8
 NA3D_ERR_CONFIG = -9
 NA3D_ERR_STRIDE = -10
+NA3D_ERR_BOX = -11
 
 EXPORTS = ("na3d_fwd", "na3d_check_args", "na3d_status_string", "na3d_plan",
            "na3d_fwd_config", "na3d_plan_config", "na3d_fwd_strided", "na3d_check_args_strided",
-           "na3d_fwd_strided_config", "na3d_num_variants", "na3d_abi_version")
+           "na3d_fwd_strided_config", "na3d_fwd_subgrid", "na3d_check_args_subgrid",
+           "na3d_fwd_subgrid_config", "na3d_num_variants", "na3d_abi_version")
 PLAN_KEYS = ("family", "tile_t", "tile_h", "tile_w", "workgroups", "threads", "lds_bytes",
              "planes", "variant", "runs")
 
@@ -78,6 +80,13 @@ def load(path: str = LIB_PATH):
         lib.na3d_check_args_strided.restype = i32
         lib.na3d_fwd_strided_config.argtypes = [p, p, p, p] + [i32] * 9 + [ll] + [i32] * 3 + [p]
         lib.na3d_fwd_strided_config.restype = i32
+        ip = ctypes.POINTER(i32)
+        lib.na3d_fwd_subgrid.argtypes = [p, p, p, p] + [i32] * 9 + [ip, ll, p]
+        lib.na3d_fwd_subgrid.restype = i32
+        lib.na3d_check_args_subgrid.argtypes = [p, p, p, p] + [i32] * 9 + [ip, ll]
+        lib.na3d_check_args_subgrid.restype = i32
+        lib.na3d_fwd_subgrid_config.argtypes = [p, p, p, p] + [i32] * 9 + [ip, ll] + [i32] * 3 + [p]
+        lib.na3d_fwd_subgrid_config.restype = i32
         lib.na3d_num_variants.argtypes = []
         lib.na3d_num_variants.restype = i32
         lib.na3d_abi_version.argtypes = []
@@ -115,6 +124,18 @@ def check_args_strided(q_ptr, k_ptr, v_ptr, out_ptr, shape, kernel_size, strides
                                           KT, KH, KW, _stride_array(strides))
 
 
+def check_args_subgrid(q_ptr, k_ptr, v_ptr, out_ptr, shape, kernel_size, box, strides=None) -> int:
+    """Host-only argument check of the query-box entry point.  ``shape`` is the
+    k/v grid, ``box`` = (t0, h0, w0, Tq, Hq, Wq), ``strides`` as for
+    check_args_strided or None for contiguous tensors."""
+    B, T, H, W, NH, HD = (int(x) for x in shape)
+    KT, KH, KW = (int(x) for x in kernel_size)
+    bx = (ctypes.c_int * 6)(*[int(x) for x in box])
+    st = None if strides is None else _stride_array(strides)
+    return load().na3d_check_args_subgrid(q_ptr, k_ptr, v_ptr, out_ptr, B, T, H, W, NH, HD,
+                                          KT, KH, KW, bx, st)
+
+
 def plan(shape, kernel_size, family: int = 0, variant: int = 0, tile_t: int = 0) -> dict:
     """Launch plan for these sizes (automatic, or an explicit configuration)."""
     B, T, H, W, NH, HD = (int(x) for x in shape)
@@ -132,14 +153,20 @@ def num_variants() -> int:
 
 
 def fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, shape, kernel_size,
-            stream: int = 0, config=None, strides=None) -> None:
+            stream: int = 0, config=None, strides=None, box=None) -> None:
     """Call na3d_fwd (or na3d_fwd_config when ``config`` = (family, variant,
     tile_t) is given; the strided entry points when ``strides`` = four
     (sB, sT, sH, sW, sN) element-stride tuples for q, k, v, out is given) on
     raw device addresses; raises NA3DError on failure."""
     B, T, H, W, NH, HD = (int(x) for x in shape)
     KT, KH, KW = (int(x) for x in kernel_size)
-    if strides is not None:
+    if box is not None:
+        bx = (ctypes.c_int * 6)(*[int(x) for x in box])
+        st = None if strides is None else _stride_array(strides)
+        fam, var, tt = (0, 0, 0) if config is None else (int(x) for x in config)
+        rc = load().na3d_fwd_subgrid_config(q_ptr, k_ptr, v_ptr, out_ptr, B, T, H, W, NH, HD,
+                                            KT, KH, KW, bx, st, fam, var, tt, stream)
+    elif strides is not None:
         st = _stride_array(strides)
         if config is None:
             rc = load().na3d_fwd_strided(q_ptr, k_ptr, v_ptr, out_ptr, B, T, H, W, NH, HD, KT,
@@ -199,4 +226,46 @@ def fwd(q, k, v, kernel_size, out=None, config=None):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), q.shape,
                 kernel_size, stream, config, strides)
+    return out
+
+
+def fwd_subgrid(q, k, v, kernel_size, offset, out=None, config=None):
+    """Neighborhood attention for the queries of a sub-box of the grid, with
+    windows placed in the whole grid.
+
+    k, v: (B,T,H,W,NH,HD), the whole grid.  q (and out): (B,Tq,Hq,Wq,NH,HD),
+    the queries at grid positions offset + (i, j, l), offset = (t0, h0, w0).
+    The result equals the same box of ``fwd`` over the whole grid.  Strided
+    views are accepted as in ``fwd``.  Returns ``out``.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.device.type != "cuda":
+            raise TypeError("%s must be a bfloat16 GPU tensor" % name)
+        if t.dim() != 6:
+            raise ValueError("expected (B,T,H,W,NH,HD) tensors, got %d dims for %s" % (t.dim(), name))
+        if t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError("%s must have a contiguous last (head-dim) axis" % name)
+    if k.shape != v.shape:
+        raise ValueError("k and v shapes differ: %s %s" % (k.shape, v.shape))
+    if q.shape[0] != k.shape[0] or q.shape[4:] != k.shape[4:]:
+        raise ValueError("q %s does not match the batch/heads/head dim of k %s" % (q.shape, k.shape))
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v are on different devices")
+    t0, h0, w0 = (int(x) for x in offset)
+    box = (t0, h0, w0, q.shape[1], q.shape[2], q.shape[3])
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    elif (out.shape != q.shape or out.dtype != torch.bfloat16 or out.device != q.device
+          or (out.shape[-1] > 1 and out.stride(-1) != 1)):
+        raise ValueError("out must be a bf16 tensor shaped like q with a contiguous last axis")
+    tensors = (q, k, v, out)
+    strides = None
+    if not all(t.is_contiguous() for t in tensors):
+        strides = [tuple(int(x) for x in t.stride()[:5]) for t in tensors]
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), k.shape,
+                kernel_size, stream, config, strides, box)
     return out

@@ -71,13 +71,22 @@ struct Strides {
   int64_t b, t, h, w, n;
 };
 
+// The query box: q and out hold queries [t0, t0+Tq) x [h0, h0+Hq) x
+// [w0, w0+Wq) of the T x H x W grid of k and v, and every window is placed
+// in that full grid (the whole grid: offsets 0, extents T, H, W).
+struct Box {
+  int t0, h0, w0;
+  int Tq, Hq, Wq;
+};
+
 struct Problem {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
-  int B, T, H, W, NH;
+  int B, T, H, W, NH;      // k and v grid
   int KT, KH, KW;
+  Box box;                 // q and out
   Strides sq, sk, sv, so;  // k and v share h, w and n
 };
 

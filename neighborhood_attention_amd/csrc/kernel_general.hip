@@ -36,8 +36,10 @@ struct GeneralArgs {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
-  int B, T, H, W, NH;
+  int B, T, H, W, NH;  // k and v grid
   int KT, KH, KW;
+  int t_off, h_off, w_off;  // query box: q/out plane t is grid plane t_off + t, ...
+  int Tq, Hq, Wq;           // ... and its extents
   int tiles_h, tiles_w;
   int lds_rows;  // capacity of each of the K and V staging buffers, in rows
   Strides sq, sk, sv, so;  // element strides; k and v share h, w and n
@@ -86,8 +88,8 @@ na3d_fwd_general_kernel(const GeneralArgs a) {
 
   // ---- workgroup -> (b, n, tile_h, tile_w, t); t varies fastest
   int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int t = wg % a.T;
-  wg /= a.T;
+  const int t = wg % a.Tq;  // query plane in the box
+  wg /= a.Tq;
   const int tw = wg % a.tiles_w;
   wg /= a.tiles_w;
   const int th = wg % a.tiles_h;
@@ -95,34 +97,37 @@ na3d_fwd_general_kernel(const GeneralArgs a) {
   const int n = wg % a.NH;
   const int b = wg / a.NH;
 
-  const int H = a.H, W = a.W, KH = a.KH, KW = a.KW;
+  const int H = a.H, W = a.W, KH = a.KH, KW = a.KW, Hq = a.Hq, Wq = a.Wq;
+  // queries are indexed in the box, windows and K/V in the grid
+  auto wsh = [&](int h) { return win_start(a.h_off + h, KH, H); };
+  auto wsw = [&](int w) { return win_start(a.w_off + w, KW, W); };
   const int h0 = th * BH, w0 = tw * BW;
-  const int h1 = min(h0 + BH, H) - 1, w1 = min(w0 + BW, W) - 1;
-  // halo of the whole tile (global coordinates), [hh0, hh0+hhn) x [hw0, hw0+hwd)
-  const int hh0 = win_start(h0, KH, H);
-  const int hhn = win_start(h1, KH, H) + KH - hh0;
-  const int hw0 = win_start(w0, KW, W);
-  const int hwd = win_start(w1, KW, W) + KW - hw0;
+  const int h1 = min(h0 + BH, Hq) - 1, w1 = min(w0 + BW, Wq) - 1;
+  // halo of the whole tile (grid coordinates), [hh0, hh0+hhn) x [hw0, hw0+hwd)
+  const int hh0 = wsh(h0);
+  const int hhn = wsh(h1) + KH - hh0;
+  const int hw0 = wsw(w0);
+  const int hwd = wsw(w1) + KW - hw0;
   const int halo_rows = hhn * hwd;
-  const int st = win_start(t, a.KT, a.T);
+  const int st = win_start(a.t_off + t, a.KT, a.T);
 
   // ---- this wave's 16-query block
   const int bh0 = h0 + (wave / WW) * QH;
   const int bw0 = w0 + (wave % WW) * QW;
-  const bool wave_active = bh0 < H && bw0 < W;
-  const int bh1 = min(bh0 + QH, H) - 1;
-  const int bw1 = min(bw0 + QW, W) - 1;
+  const bool wave_active = bh0 < Hq && bw0 < Wq;
+  const int bh1 = min(bh0 + QH, Hq) - 1;
+  const int bw1 = min(bw0 + QW, Wq) - 1;
   const int qh = bh0 + q16 / QW;
   const int qw = bw0 + q16 % QW;
-  const bool qvalid = wave_active && qh < H && qw < W;
-  const int qhc = min(qh, H - 1), qwc = min(qw, W - 1);
-  const int ash = win_start(qhc, KH, H);  // query window start (global)
-  const int asw = win_start(qwc, KW, W);
-  // union of the block's windows, in global coordinates
-  const int uh0 = wave_active ? win_start(bh0, KH, H) : hh0;
-  const int uhn = wave_active ? win_start(bh1, KH, H) + KH - uh0 : 0;
-  const int uw0 = wave_active ? win_start(bw0, KW, W) : hw0;
-  const int uw = wave_active ? win_start(bw1, KW, W) + KW - uw0 : 1;
+  const bool qvalid = wave_active && qh < Hq && qw < Wq;
+  const int qhc = min(qh, Hq - 1), qwc = min(qw, Wq - 1);
+  const int ash = wsh(qhc);  // query window start (grid)
+  const int asw = wsw(qwc);
+  // union of the block's windows, in grid coordinates
+  const int uh0 = wave_active ? wsh(bh0) : hh0;
+  const int uhn = wave_active ? wsh(bh1) + KH - uh0 : 0;
+  const int uw0 = wave_active ? wsw(bw0) : hw0;
+  const int uw = wave_active ? wsw(bw1) + KW - uw0 : 1;
   const int oh = uh0 - hh0, ow = uw0 - hw0;  // union origin inside the halo
 
 
@@ -304,6 +309,8 @@ int launch_general(const Problem& p, const Launch& l, int hd, hipStream_t s) {
   GeneralArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o;
   a.B = p.B; a.T = p.T; a.H = p.H; a.W = p.W; a.NH = p.NH;
+  a.t_off = p.box.t0; a.h_off = p.box.h0; a.w_off = p.box.w0;
+  a.Tq = p.box.Tq; a.Hq = p.box.Hq; a.Wq = p.box.Wq;
   a.KT = p.KT; a.KH = p.KH; a.KW = p.KW;
   a.tiles_h = l.tiles_h;
   a.tiles_w = l.tiles_w;

@@ -72,8 +72,10 @@ struct RollArgs {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
-  int B, T, H, W, NH;
+  int B, T, H, W, NH;  // k and v grid
   int KT, KH, KW;
+  int t_off, h_off, w_off;  // query box: q/out plane t is grid plane t_off + t, ...
+  int Tq, Hq, Wq;           // ... and its extents
   int tiles_t, tiles_h, tiles_w;
   int tc;        // query planes per middle run
   int ta;        // first run [0, ta); 0 = none
@@ -273,45 +275,50 @@ na3d_fwd_roll_kernel(const RollArgs a) {
   const int b = wg / a.NH;
 
   const int T = a.T, H = a.H, W = a.W, KT = a.KT, KH = a.KH, KW = a.KW;
+  const int Hq = a.Hq, Wq = a.Wq;
+  // Queries are indexed in the box (q, out, tiles, runs); windows, halos and
+  // K/V in the grid: the window of box plane t starts at key plane wst(t),
+  // of box row h at grid row wsh(h), of box column w at grid column wsw(w).
+  auto wst = [&](int t) { return win_start(a.t_off + t, KT, T); };
+  auto wsh = [&](int h) { return win_start(a.h_off + h, KH, H); };
+  auto wsw = [&](int w) { return win_start(a.w_off + w, KW, W); };
   // query planes [t0, t1) of run ri
   auto run_bounds = [&](int ri, int& t0, int& t1) {
     const int mid = ri - (a.ta > 0 ? 1 : 0);
     if (a.ta > 0 && ri == 0) {
       t0 = 0;
       t1 = a.ta;
-    } else if (a.tz < T && ri == a.nruns - 1) {
+    } else if (a.tz < a.Tq && ri == a.nruns - 1) {
       t0 = a.tz;
-      t1 = T;
+      t1 = a.Tq;
     } else {
       t0 = a.ta + mid * a.tc;
       t1 = min(t0 + a.tc, a.tz);
     }
   };
   const int r_lo = tt * a.rpw, r_hi = min(r_lo + a.rpw, a.nruns);
-  const int h0 = th * BH, w0 = tw * QW;
-  const int h1 = min(h0 + BH, H) - 1, w1 = min(w0 + QW, W) - 1;
-  // halo of the tile: rows [hh0, hh0 + hhn) x columns [hw0, hw0 + hwd)
-  const int hh0 = win_start(h0, KH, H);
-  const int hhn = win_start(h1, KH, H) + KH - hh0;
-  const int hw0 = win_start(w0, KW, W);
-  const int hwd = win_start(w1, KW, W) + KW - hw0;
+  const int h0 = th * BH, w0 = tw * QW;  // tile origin in the box
+  const int h1 = min(h0 + BH, Hq) - 1, w1 = min(w0 + QW, Wq) - 1;
+  // halo of the tile (grid coordinates): rows [hh0, hh0 + hhn) x columns
+  // [hw0, hw0 + hwd)
+  const int hh0 = wsh(h0);
+  const int hhn = wsh(h1) + KH - hh0;
+  const int hw0 = wsw(w0);
+  const int hwd = wsw(w1) + KW - hw0;
   const int halo_rows = hhn * hwd;
   const int total_chunks = halo_rows * CPR;
 
   // ---- this wave's block of 16 queries
   const int bh0 = h0 + ih * QH;
-  const bool active = bh0 < H;
-  const int bh1 = min(bh0 + QH, H) - 1;
+  const bool active = bh0 < Hq;
   const int qh = bh0 + q16 / QW;
   const int qw = w0 + q16 % QW;
-  const bool qvalid = active && qh < H && qw < W;
-  const int qhc = min(qh, H - 1), qwc = min(qw, W - 1);
-  const int ash = win_start(qhc, KH, H);
-  const int asw = win_start(qwc, KW, W);
+  const bool qvalid = active && qh < Hq && qw < Wq;
+  const int qhc = min(qh, Hq - 1), qwc = min(qw, Wq - 1);
   // union of the block's windows = staged rows [base, base + un); the wave
   // reads rows [rb, rb + NG * GK), which hold the union (the host checks
   // NG * GK >= un) and stay in the buffer (lds_rows >= NG * GK)
-  const int uh0 = bh0 < H ? win_start(bh0, KH, H) : hh0;
+  const int uh0 = active ? wsh(bh0) : hh0;
   const int base = (uh0 - hh0) * hwd;
   const int rb = max(0, min(base, a.lds_rows - NG * GK));
 
@@ -325,9 +332,9 @@ na3d_fwd_roll_kernel(const RollArgs a) {
   for (int j = 0; j < 4; ++j) {
     const int qi = 4 * g + j;
     const int qhj = bh0 + qi / QW, qwj = w0 + qi % QW;
-    const bool ok = active && qhj < H && qwj < W;
-    ah[j] = ok ? win_start(qhj, KH, H) - hh0 : -(1 << 20);
-    aw[j] = win_start(min(qwj, W - 1), KW, W) - hw0;
+    const bool ok = active && qhj < Hq && qwj < Wq;
+    ah[j] = ok ? wsh(qhj) - hh0 : -(1 << 20);
+    aw[j] = wsw(min(qwj, Wq - 1)) - hw0;
   }
   const int kp = key_perm(HD, q16);
   constexpr int NKP = (NK + 1) / 2;  // tile pairs per group
@@ -471,21 +478,21 @@ na3d_fwd_roll_kernel(const RollArgs a) {
   bool pend_on = false;
   int t0, t1;
   run_bounds(r_lo, t0, t1);
-  issue_stage(win_start(t0, KT, T), 0);  // step st uses buffer st % NBUF
+  issue_stage(wst(t0), 0);  // step st uses buffer st % NBUF
   int st = 0;
   for (int ri = r_lo; ri < r_hi; ++ri) {
     if (ri > r_lo) run_bounds(ri, t0, t1);
-    const int p0 = win_start(t0, KT, T), p1 = win_start(t1 - 1, KT, T) + KT;
+    const int p0 = wst(t0), p1 = wst(t1 - 1) + KT;  // the run's key planes
     int nt0 = 0, nt1 = 0, np0 = -1;  // the next run, whose first plane follows p1 - 1
     if (ri + 1 < r_hi) {
       run_bounds(ri + 1, nt0, nt1);
-      np0 = win_start(nt0, KT, T);
+      np0 = wst(nt0);
     }
     auto tq = [&](int j) { return t0 + it + WT * j; };
     int jlo = 0, jhi = -1;  // query planes j in [jlo, jhi] are in flight
     for (int tp = p0; tp < p1; ++tp, ++st) {
       // admit this wave's query planes whose window starts here
-      while (tq(jhi + 1) < t1 && win_start(tq(jhi + 1), KT, T) <= tp) {
+      while (tq(jhi + 1) < t1 && wst(tq(jhi + 1)) <= tp) {
         ++jhi;
         const int sl = jhi % NS;
 #pragma unroll
@@ -515,8 +522,8 @@ na3d_fwd_roll_kernel(const RollArgs a) {
       {
         int tn = -1;
         if (tp + 1 < p1) {
-          if (tq(jhi + 1) < t1 && win_start(tq(jhi + 1), KT, T) == tp + 1) tn = tq(jhi + 1);
-        } else if (np0 >= 0 && nt0 + it < nt1 && win_start(nt0 + it, KT, T) == np0) {
+          if (tq(jhi + 1) < t1 && wst(tq(jhi + 1)) == tp + 1) tn = tq(jhi + 1);
+        } else if (np0 >= 0 && nt0 + it < nt1 && wst(nt0 + it) == np0) {
           tn = nt0 + it;
         }
         if (tn >= 0) {
@@ -650,7 +657,7 @@ na3d_fwd_roll_kernel(const RollArgs a) {
       // retire this wave's query planes whose window ends here; the output
       // waits in registers for the next barrier (a second one in the same
       // plane is stored at once)
-      while (jlo <= jhi && win_start(tq(jlo), KT, T) + KT - 1 == tp) {
+      while (jlo <= jhi && wst(tq(jlo)) + KT - 1 == tp) {
         const int sl = jlo % NS;
         if (active) {
           if (pend_on && qvalid) store_out<MT>(pend_p, pend, g);
@@ -690,6 +697,8 @@ int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s) {
   RollArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o;
   a.B = p.B; a.T = p.T; a.H = p.H; a.W = p.W; a.NH = p.NH;
+  a.t_off = p.box.t0; a.h_off = p.box.h0; a.w_off = p.box.w0;
+  a.Tq = p.box.Tq; a.Hq = p.box.Hq; a.Wq = p.box.Wq;
   a.KT = p.KT; a.KH = p.KH; a.KW = p.KW;
   a.tiles_t = l.tiles_t;
   a.tiles_h = l.tiles_h;

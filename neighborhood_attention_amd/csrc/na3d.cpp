@@ -66,71 +66,55 @@ int64_t kv_span_bytes(const Strides& sk, int H, int W, int HD) {
   return 2 * ((int64_t)(H - 1) * sk.h + (int64_t)(W - 1) * sk.w + HD);
 }
 
-// Stride contract of the strided entry points; st = {q, k, v, out}.
-int check_strides(const void* q, const void* k, const void* v, const void* out, int B, int T,
-                  int H, int W, int NH, int HD, const Strides* st) {
-  const int64_t lim = (int64_t)1 << 56;
-  for (int i = 0; i < 4; ++i) {
-    const int64_t x[5] = {st[i].b, st[i].t, st[i].h, st[i].w, st[i].n};
-    for (int j = 0; j < 5; ++j)
-      if (x[j] < 0 || x[j] % 8 != 0 || x[j] > lim) return NA3D_ERR_STRIDE;
-  }
-  if (st[1].h != st[2].h || st[1].w != st[2].w || st[1].n != st[2].n) return NA3D_ERR_STRIDE;
-  // no two elements of out at one address: ordered by stride, every axis of
-  // extent > 1 steps over the whole span of the smaller ones (HD first)
-  {
-    int64_t ext[5] = {B, T, H, W, NH};
-    int64_t str[5] = {st[3].b, st[3].t, st[3].h, st[3].w, st[3].n};
-    int idx[5] = {0, 1, 2, 3, 4};
-    std::sort(idx, idx + 5, [&](int a, int b) { return str[a] < str[b]; });
-    int64_t span = HD;
-    for (int j = 0; j < 5; ++j) {
-      const int a = idx[j];
-      if (ext[a] == 1) continue;
-      if (str[a] < span) return NA3D_ERR_STRIDE;
-      span = str[a] * (ext[a] - 1) + span;
-    }
-  }
-  const size_t bo = 2 * (size_t)extent(st[3], B, T, H, W, NH, HD);
-  if (overlaps2(out, bo, q, 2 * (size_t)extent(st[0], B, T, H, W, NH, HD)) ||
-      overlaps2(out, bo, k, 2 * (size_t)extent(st[1], B, T, H, W, NH, HD)) ||
-      overlaps2(out, bo, v, 2 * (size_t)extent(st[2], B, T, H, W, NH, HD)))
-    return NA3D_ERR_OVERLAP;
-  return NA3D_OK;
-}
+// Everything a plan depends on: the k/v grid, heads, head dim, window, the
+// query box, and the bytes spanned by one head's spatial K/V plane.
+struct Geom {
+  int B, T, H, W, NH, HD, KT, KH, KW;
+  Box box;
+  int64_t kv_span;
+};
 
-// Query-plane runs along T: an optional first run [0, ta) (the planes whose
-// window is [0, KT)), middle runs of tc planes over [ta, tz), and an optional
-// last run [tz, T) (the planes whose window is [T - KT, T)).
+// The T axis of the query box: local query plane tl is plane off + tl of the
+// grid, and its window starts at key plane ws(tl).
+struct TAxis {
+  int n;  // query planes
+  int off, T, KT;
+  int ws(int tl) const { return win_start(off + tl, KT, T); }
+};
+
+// Query-plane runs along the box's T axis (local indices): an optional first
+// run [0, ta) (the planes whose window is [0, KT)), middle runs of tc planes
+// over [ta, tz), and an optional last run [tz, n) (the planes whose window is
+// [T - KT, T)).
 struct Runs {
   int ta, tz, tc;
 };
 
-int run_count(int T, const Runs& r) {
-  return (r.ta > 0) + (r.tz > r.ta ? ceil_div(r.tz - r.ta, r.tc) : 0) + (r.tz < T);
+int run_count(const TAxis& ax, const Runs& r) {
+  return (r.ta > 0) + (r.tz > r.ta ? ceil_div(r.tz - r.ta, r.tc) : 0) + (r.tz < ax.n);
 }
 
 // Calls f(t0, t1) for every run.
 template <class F>
-void for_runs(int T, const Runs& r, F f) {
+void for_runs(const TAxis& ax, const Runs& r, F f) {
   if (r.ta > 0) f(0, r.ta);
   for (int t0 = r.ta; t0 < r.tz; t0 += r.tc) f(t0, std::min(t0 + r.tc, r.tz));
-  if (r.tz < T) f(r.tz, T);
+  if (r.tz < ax.n) f(r.tz, ax.n);
 }
 
 // Most query planes one wave holds at a time: in a run [t0, t1) wave r of WT
 // owns t0 + r, t0 + r + WT, ...; count, over all key planes of the run, the
 // owned query planes whose window contains that key plane.
-int max_active_per_wave(int T, int KT, const Runs& runs, int wt) {
+int max_active_per_wave(const TAxis& ax, const Runs& runs, int wt) {
   int best = 0;
-  for_runs(T, runs, [&](int t0, int t1) {
-    const int p0 = win_start(t0, KT, T), p1 = win_start(t1 - 1, KT, T) + KT;
+  for_runs(ax, runs, [&](int t0, int t1) {
+    const int p0 = ax.ws(t0), p1 = ax.ws(t1 - 1) + ax.KT;
     for (int r = 0; r < wt; ++r)
       for (int tp = p0; tp < p1; ++tp) {
         int c = 0;
         for (int t = t0 + r; t < t1; t += wt) {
-          const int s = win_start(t, KT, T);
-          c += (s <= tp && tp < s + KT);
+          const int s = ax.ws(t);
+          c += (s <= tp && tp < s + ax.KT);
         }
         best = std::max(best, c);
       }
@@ -139,11 +123,11 @@ int max_active_per_wave(int T, int KT, const Runs& runs, int wt) {
 }
 
 // K/V planes staged per spatial tile over all runs, and the most in one run.
-void staged_planes(int T, int KT, const Runs& runs, int* total, int* most) {
+void staged_planes(const TAxis& ax, const Runs& runs, int* total, int* most) {
   *total = 0;
   *most = 0;
-  for_runs(T, runs, [&](int t0, int t1) {
-    const int n = win_start(t1 - 1, KT, T) + KT - win_start(t0, KT, T);
+  for_runs(ax, runs, [&](int t0, int t1) {
+    const int n = ax.ws(t1 - 1) + ax.KT - ax.ws(t0);
     *total += n;
     *most = std::max(*most, n);
   });
@@ -153,26 +137,26 @@ void staged_planes(int T, int KT, const Runs& runs, int* total, int* most) {
 // tile_t > 0 fixes the middle run length.  Both layouts are tried: with the
 // shared-window planes split off into runs of their own, and without; the
 // feasible one that stages fewer planes wins.
-bool choose_runs(int T, int KT, int wt, int ns, int tile_t, Runs* out) {
+bool choose_runs(const TAxis& ax, int wt, int ns, int tile_t, Runs* out) {
   int ta = 0;
-  while (ta < T && win_start(ta, KT, T) == 0) ++ta;
-  int tz = T;
-  while (tz > 0 && win_start(tz - 1, KT, T) == T - KT) --tz;
+  while (ta < ax.n && ax.ws(ta) == 0) ++ta;
+  int tz = ax.n;
+  while (tz > 0 && ax.ws(tz - 1) == ax.T - ax.KT) --tz;
   bool found = false;
   int best_cost = 0;
   for (int split = 1; split >= 0; --split) {
     Runs r;
     r.ta = split ? ta : 0;
-    r.tz = split ? std::max(tz, ta) : T;
-    if (split && (ta >= T || r.tz <= 0)) continue;  // one shared window: nothing to split
+    r.tz = split ? std::max(tz, ta) : ax.n;
+    if (split && (ta >= ax.n || r.tz <= 0)) continue;  // one shared window: nothing to split
     const int span = std::max(r.tz - r.ta, 1);
     int tc = tile_t > 0 ? std::min(tile_t, span) : span;
     r.tc = tc;
     if (tile_t <= 0)
-      while (tc > 1 && max_active_per_wave(T, KT, r, wt) > ns) r.tc = --tc;
-    if (max_active_per_wave(T, KT, r, wt) > ns) continue;
+      while (tc > 1 && max_active_per_wave(ax, r, wt) > ns) r.tc = --tc;
+    if (max_active_per_wave(ax, r, wt) > ns) continue;
     int total, most;
-    staged_planes(T, KT, r, &total, &most);
+    staged_planes(ax, r, &total, &most);
     if (!found || total < best_cost) {
       found = true;
       best_cost = total;
@@ -182,39 +166,38 @@ bool choose_runs(int T, int KT, int wt, int ns, int tile_t, Runs* out) {
   return found;
 }
 
-bool plan_general(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, Launch* l) {
+bool plan_general(const Geom& g, Launch* l) {
   const int BH = general_tile_h(), BW = general_tile_w();
   l->family = 1;
   l->variant = 0;
   l->tile_t = 1;
   l->tile_h = BH;
   l->tile_w = BW;
-  l->tiles_t = T;
+  l->tiles_t = g.box.Tq;
   l->ta = 0;
-  l->tz = T;
-  l->nruns = T;
+  l->tz = g.box.Tq;
+  l->nruns = g.box.Tq;
   l->rpw = 1;
-  l->tiles_h = ceil_div(H, BH);
-  l->tiles_w = ceil_div(W, BW);
-  l->wgs = (int64_t)B * NH * T * l->tiles_h * l->tiles_w;
+  l->tiles_h = ceil_div(g.box.Hq, BH);
+  l->tiles_w = ceil_div(g.box.Wq, BW);
+  l->wgs = (int64_t)g.B * g.NH * g.box.Tq * l->tiles_h * l->tiles_w;
   l->threads = general_threads();
-  const int row = general_row_bytes(HD);
-  const int max_halo = std::min(BH + KH - 1, H) * std::min(BW + KW - 1, W);
+  const int row = general_row_bytes(g.HD);
+  const int max_halo = std::min(BH + g.KH - 1, g.H) * std::min(BW + g.KW - 1, g.W);
   l->lds_rows = std::min(max_halo, kGeneralLdsBytes / (2 * row));
   l->lds_bytes = 2 * l->lds_rows * row;
-  l->planes = KT;
-  (void)KW;
+  l->planes = g.KT;
   return l->wgs <= 0x7fffffff;
 }
 
 // Can rolling variant v run these sizes?  tile_t = 0 picks the run length.
-bool plan_roll(int v, int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
-               int tile_t, int64_t kv_span, Launch* l) {
+bool plan_roll(int v, const Geom& g, int tile_t, Launch* l) {
   if (v < 0 || v >= kNumRollVariants) return false;
   const RollVariant& rv = kRollVariants[v];
+  const int HD = g.HD, KH = g.KH, KW = g.KW, H = g.H, W = g.W;
   if (rv.hd != HD) return false;
   // staging offsets are 32-bit byte offsets within one head's K/V plane
-  if (kv_span >= ((int64_t)1 << 32)) return false;
+  if (g.kv_span >= ((int64_t)1 << 32)) return false;
   const int BH = rv.wh * rv.qh;
   const int hwd_max = std::min(rv.qw + KW - 1, W);
   const int un_max = std::min(rv.qh + KH - 1, H) * hwd_max;
@@ -226,25 +209,26 @@ bool plan_roll(int v, int B, int T, int H, int W, int NH, int HD, int KT, int KH
   // K and V rows of HD*2 bytes, in one or two plane buffers
   const int64_t lds = 2LL * rv.nbuf * rows * (HD * 2);
   if (lds > kMaxLdsBytes) return false;
-  const int tiles_h = ceil_div(H, BH), tiles_w = ceil_div(W, rv.qw);
-  const int64_t spatial = (int64_t)B * NH * tiles_h * tiles_w;
+  const int tiles_h = ceil_div(g.box.Hq, BH), tiles_w = ceil_div(g.box.Wq, rv.qw);
+  const int64_t spatial = (int64_t)g.B * g.NH * tiles_h * tiles_w;
+  const TAxis ax{g.box.Tq, g.box.t0, g.T, g.KT};
   Runs r;
-  if (!choose_runs(T, KT, rv.wt, rv.ns, tile_t, &r)) return false;
+  if (!choose_runs(ax, rv.wt, rv.ns, tile_t, &r)) return false;
   if (tile_t <= 0) {
     // shorter middle runs while the grid is too small to fill the chip
-    while (r.tc > rv.wt && spatial * run_count(T, r) < kTargetWorkgroups) {
+    while (r.tc > rv.wt && spatial * run_count(ax, r) < kTargetWorkgroups) {
       Runs s = r;
       s.tc = ceil_div(r.tc, 2);
-      if (max_active_per_wave(T, KT, s, rv.wt) > rv.ns) break;
+      if (max_active_per_wave(ax, s, rv.wt) > rv.ns) break;
       r = s;
     }
   }
   int total, most;
-  staged_planes(T, KT, r, &total, &most);
+  staged_planes(ax, r, &total, &most);
   // a workgroup streams several consecutive runs (one set-up, and the next
   // run's first plane is fetched during the last plane of the previous one)
   // as long as the grid keeps enough workgroups
-  const int nruns = run_count(T, r);
+  const int nruns = run_count(ax, r);
   const int groups = (int)std::min<int64_t>(nruns, std::max<int64_t>(1, (kTargetWorkgroups + spatial - 1) / spatial));
   const int rpw = ceil_div(nruns, groups);
   l->family = 2;
@@ -270,8 +254,7 @@ bool plan_roll(int v, int B, int T, int H, int W, int NH, int HD, int KT, int KH
 // Preferred rolling instantiations, best first (from measured sweeps), by
 // head dimension and by the union of one 2x8 query block's windows; the first
 // whose static limits fit the sizes wins.
-int pick_roll(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, int64_t kv_span,
-              Launch* l) {
+int pick_roll(const Geom& g, Launch* l) {
   static const int p16[] = {11};
   static const int p32[] = {12};
   static const int p64_small[] = {8, 34, 21, 26, 20, 9};       // union <= 64 keys
@@ -279,10 +262,10 @@ int pick_roll(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW
   static const int p64_large[] = {5, 10, 22, 6, 7, 9};     // larger windows
   static const int p128[] = {25, 15, 14, 13, 16, 29};
   static const int p256[] = {17};
-  const int un28 = std::min(2 + KH - 1, H) * std::min(8 + KW - 1, W);
+  const int un28 = std::min(2 + g.KH - 1, g.H) * std::min(8 + g.KW - 1, g.W);
   const int* pref;
   int np;
-  switch (HD) {
+  switch (g.HD) {
     case 16: pref = p16; np = 1; break;
     case 32: pref = p32; np = 1; break;
     case 64:
@@ -298,39 +281,21 @@ int pick_roll(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW
     default: pref = p256; np = 1; break;
   }
   for (int i = 0; i < np; ++i)
-    if (plan_roll(pref[i], B, T, H, W, NH, HD, KT, KH, KW, 0, kv_span, l)) return 1;
+    if (plan_roll(pref[i], g, 0, l)) return 1;
   return 0;
 }
 
-int make_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, int64_t kv_span,
-              Launch* l) {
-  if (pick_roll(B, T, H, W, NH, HD, KT, KH, KW, kv_span, l)) return NA3D_OK;
-  if (plan_general(B, T, H, W, NH, HD, KT, KH, KW, l)) return NA3D_OK;
+int make_plan(const Geom& g, Launch* l) {
+  if (pick_roll(g, l)) return NA3D_OK;
+  if (plan_general(g, l)) return NA3D_OK;
   return NA3D_ERR_SHAPE;
 }
 
-int make_plan_config(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
-                     int family, int variant, int tile_t, int64_t kv_span, Launch* l) {
-  if (family == 0) return make_plan(B, T, H, W, NH, HD, KT, KH, KW, kv_span, l);
-  if (family == 1)
-    return plan_general(B, T, H, W, NH, HD, KT, KH, KW, l) ? NA3D_OK : NA3D_ERR_SHAPE;
-  if (family == 2)
-    return plan_roll(variant, B, T, H, W, NH, HD, KT, KH, KW, tile_t, kv_span, l) ? NA3D_OK
-                                                                                   : NA3D_ERR_CONFIG;
+int make_plan_config(const Geom& g, int family, int variant, int tile_t, Launch* l) {
+  if (family == 0) return make_plan(g, l);
+  if (family == 1) return plan_general(g, l) ? NA3D_OK : NA3D_ERR_SHAPE;
+  if (family == 2) return plan_roll(variant, g, tile_t, l) ? NA3D_OK : NA3D_ERR_CONFIG;
   return NA3D_ERR_CONFIG;
-}
-
-void fill_plan(const Launch& l, int* plan) {
-  plan[0] = l.family;
-  plan[1] = l.tile_t;
-  plan[2] = l.tile_h;
-  plan[3] = l.tile_w;
-  plan[4] = (int)l.wgs;
-  plan[5] = l.threads;
-  plan[6] = l.lds_bytes;
-  plan[7] = l.planes;
-  plan[8] = l.variant;
-  plan[9] = l.tiles_t;
 }
 
 // gfx950 check, cached per device (0 unknown, 1 yes, -1 no)
@@ -350,8 +315,69 @@ int device_ok() {
   return st == 1 ? NA3D_OK : NA3D_ERR_DEVICE;
 }
 
-int run(const void* q, const void* k, const void* v, void* out, int B, int T, int H, int W,
-        int NH, int HD, int KT, int KH, int KW, const Strides* st, const Launch& l, void* stream) {
+// Stride contract of the strided entry points; st = {q, k, v, out}.  q and
+// out have the query box's extents, k and v the grid's.
+int check_strides(const void* q, const void* k, const void* v, const void* out, const Geom& g,
+                  const Strides* st) {
+  const int64_t lim = (int64_t)1 << 56;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t x[5] = {st[i].b, st[i].t, st[i].h, st[i].w, st[i].n};
+    for (int j = 0; j < 5; ++j)
+      if (x[j] < 0 || x[j] % 8 != 0 || x[j] > lim) return NA3D_ERR_STRIDE;
+  }
+  if (st[1].h != st[2].h || st[1].w != st[2].w || st[1].n != st[2].n) return NA3D_ERR_STRIDE;
+  const Box& bx = g.box;
+  // no two elements of out at one address: ordered by stride, every axis of
+  // extent > 1 steps over the whole span of the smaller ones (HD first)
+  {
+    int64_t ext[5] = {g.B, bx.Tq, bx.Hq, bx.Wq, g.NH};
+    int64_t str[5] = {st[3].b, st[3].t, st[3].h, st[3].w, st[3].n};
+    int idx[5] = {0, 1, 2, 3, 4};
+    std::sort(idx, idx + 5, [&](int a, int b) { return str[a] < str[b]; });
+    int64_t span = g.HD;
+    for (int j = 0; j < 5; ++j) {
+      const int a = idx[j];
+      if (ext[a] == 1) continue;
+      if (str[a] < span) return NA3D_ERR_STRIDE;
+      span = str[a] * (ext[a] - 1) + span;
+    }
+  }
+  const size_t bq = 2 * (size_t)extent(st[0], g.B, bx.Tq, bx.Hq, bx.Wq, g.NH, g.HD);
+  const size_t bo = 2 * (size_t)extent(st[3], g.B, bx.Tq, bx.Hq, bx.Wq, g.NH, g.HD);
+  if (overlaps2(out, bo, q, bq) ||
+      overlaps2(out, bo, k, 2 * (size_t)extent(st[1], g.B, g.T, g.H, g.W, g.NH, g.HD)) ||
+      overlaps2(out, bo, v, 2 * (size_t)extent(st[2], g.B, g.T, g.H, g.W, g.NH, g.HD)))
+    return NA3D_ERR_OVERLAP;
+  return NA3D_OK;
+}
+
+Geom make_geom(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, const Box& box) {
+  Geom g;
+  g.B = B; g.T = T; g.H = H; g.W = W; g.NH = NH; g.HD = HD;
+  g.KT = KT; g.KH = KH; g.KW = KW;
+  g.box = box;
+  g.kv_span = 0;
+  return g;
+}
+
+Box full_box(int T, int H, int W) { return Box{0, 0, 0, T, H, W}; }
+
+// All host checks of a call, in the order the status codes document.
+int check_all(const void* q, const void* k, const void* v, const void* out, const Geom& g,
+              const Strides* st) {
+  if (!q || !k || !v || !out) return NA3D_ERR_NULL;
+  const int rc = check_sizes(g.B, g.T, g.H, g.W, g.NH, g.HD, g.KT, g.KH, g.KW);
+  if (rc != NA3D_OK) return rc;
+  const Box& b = g.box;
+  if (b.Tq < 1 || b.Hq < 1 || b.Wq < 1 || b.t0 < 0 || b.h0 < 0 || b.w0 < 0 ||
+      b.t0 > g.T - b.Tq || b.h0 > g.H - b.Hq || b.w0 > g.W - b.Wq)
+    return NA3D_ERR_BOX;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return NA3D_ERR_ALIGN;
+  return check_strides(q, k, v, out, g, st);
+}
+
+int run(const void* q, const void* k, const void* v, void* out, const Geom& g, const Strides* st,
+        const Launch& l, void* stream) {
   int rc = device_ok();
   if (rc != NA3D_OK) return rc;
   Problem p;
@@ -359,13 +385,53 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int T, in
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
   p.o = static_cast<uint16_t*>(out);
-  p.B = B; p.T = T; p.H = H; p.W = W; p.NH = NH;
-  p.KT = KT; p.KH = KH; p.KW = KW;
+  p.B = g.B; p.T = g.T; p.H = g.H; p.W = g.W; p.NH = g.NH;
+  p.KT = g.KT; p.KH = g.KH; p.KW = g.KW;
+  p.box = g.box;
   p.sq = st[0]; p.sk = st[1]; p.sv = st[2]; p.so = st[3];
   hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = l.family == 2 ? launch_roll(p, l, HD, s) : launch_general(p, l, HD, s);
+  rc = l.family == 2 ? launch_roll(p, l, g.HD, s) : launch_general(p, l, g.HD, s);
   return rc == 0 ? NA3D_OK : NA3D_ERR_LAUNCH;
 }
+
+// Checks, plans and launches one call.
+int fwd_impl(const void* q, const void* k, const void* v, void* out, Geom g, const Strides* st,
+             int family, int variant, int tile_t, void* stream) {
+  int rc = check_all(q, k, v, out, g, st);
+  if (rc != NA3D_OK) return rc;
+  g.kv_span = kv_span_bytes(st[1], g.H, g.W, g.HD);
+  Launch l;
+  rc = make_plan_config(g, family, variant, tile_t, &l);
+  if (rc != NA3D_OK) return rc;
+  return run(q, k, v, out, g, st, l, stream);
+}
+
+void read_strides(const long long* strides, Strides* st) {
+  for (int i = 0; i < 4; ++i)
+    st[i] = Strides{strides[5 * i], strides[5 * i + 1], strides[5 * i + 2], strides[5 * i + 3],
+                    strides[5 * i + 4]};
+}
+
+// Contiguous strides of q and out (box extents) and of k and v (grid extents).
+void contiguous_all(const Geom& g, Strides* st) {
+  st[0] = st[3] = contiguous(g.box.Tq, g.box.Hq, g.box.Wq, g.NH, g.HD);
+  st[1] = st[2] = contiguous(g.T, g.H, g.W, g.NH, g.HD);
+}
+
+void fill_plan(const Launch& l, int* plan) {
+  plan[0] = l.family;
+  plan[1] = l.tile_t;
+  plan[2] = l.tile_h;
+  plan[3] = l.tile_w;
+  plan[4] = (int)l.wgs;
+  plan[5] = l.threads;
+  plan[6] = l.lds_bytes;
+  plan[7] = l.planes;
+  plan[8] = l.variant;
+  plan[9] = l.tiles_t;
+}
+
+
 
 }  // namespace
 }  // namespace na3d
@@ -381,7 +447,7 @@ int na3d_num_variants(void) { return kNumRollVariants; }
 const char* na3d_status_string(int status) {
   switch (status) {
     case NA3D_OK: return "ok";
-    case NA3D_ERR_NULL: return "a tensor pointer is NULL";
+    case NA3D_ERR_NULL: return "a tensor or stride pointer is NULL";
     case NA3D_ERR_SHAPE: return "a dimension is < 1 or the tensor is too large";
     case NA3D_ERR_WINDOW: return "a window extent is < 1 or larger than its grid axis";
     case NA3D_ERR_HEAD_DIM: return "head dimension must be 16, 32, 64, 128 or 256";
@@ -393,33 +459,41 @@ const char* na3d_status_string(int status) {
     case NA3D_ERR_STRIDE:
       return "a stride is negative or not a multiple of 8, k and v differ in H/W/NH strides, "
              "or out's strides map two elements to one address";
+    case NA3D_ERR_BOX: return "the query box is empty or reaches outside the grid";
     default: return "unknown status";
   }
+}
+
+int na3d_check_args(const void* q, const void* k, const void* v, const void* out, int B,
+                    int T, int H, int W, int NH, int HD, int KT, int KH, int KW) {
+  const Geom g = make_geom(B, T, H, W, NH, HD, KT, KH, KW, full_box(T, H, W));
+  Strides st[4];
+  contiguous_all(g, st);
+  return check_all(q, k, v, out, g, st);
 }
 
 int na3d_check_args_strided(const void* q, const void* k, const void* v, const void* out, int B,
                             int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
                             const long long* strides) {
-  if (!q || !k || !v || !out || !strides) return NA3D_ERR_NULL;
-  const int rc = check_sizes(B, T, H, W, NH, HD, KT, KH, KW);
-  if (rc != NA3D_OK) return rc;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return NA3D_ERR_ALIGN;
+  if (!strides) return NA3D_ERR_NULL;
+  const Geom g = make_geom(B, T, H, W, NH, HD, KT, KH, KW, full_box(T, H, W));
   Strides st[4];
-  for (int i = 0; i < 4; ++i)
-    st[i] = Strides{strides[5 * i], strides[5 * i + 1], strides[5 * i + 2], strides[5 * i + 3],
-                    strides[5 * i + 4]};
-  return check_strides(q, k, v, out, B, T, H, W, NH, HD, st);
+  read_strides(strides, st);
+  return check_all(q, k, v, out, g, st);
 }
 
-int na3d_check_args(const void* q, const void* k, const void* v, const void* out, int B,
-                    int T, int H, int W, int NH, int HD, int KT, int KH, int KW) {
-  if (!q || !k || !v || !out) return NA3D_ERR_NULL;
-  const int rc = check_sizes(B, T, H, W, NH, HD, KT, KH, KW);
-  if (rc != NA3D_OK) return rc;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return NA3D_ERR_ALIGN;
-  const Strides c = contiguous(T, H, W, NH, HD);
-  const Strides st[4] = {c, c, c, c};
-  return check_strides(q, k, v, out, B, T, H, W, NH, HD, st);
+int na3d_check_args_subgrid(const void* q, const void* k, const void* v, const void* out, int B,
+                            int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
+                            const int* box, const long long* strides) {
+  if (!box) return NA3D_ERR_NULL;
+  const Geom g = make_geom(B, T, H, W, NH, HD, KT, KH, KW,
+                           Box{box[0], box[1], box[2], box[3], box[4], box[5]});
+  Strides st[4];
+  if (strides)
+    read_strides(strides, st);
+  else
+    contiguous_all(g, st);
+  return check_all(q, k, v, out, g, st);
 }
 
 int na3d_plan(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW, int* plan) {
@@ -431,9 +505,10 @@ int na3d_plan_config(int B, int T, int H, int W, int NH, int HD, int KT, int KH,
   if (!plan) return NA3D_ERR_NULL;
   int rc = check_sizes(B, T, H, W, NH, HD, KT, KH, KW);
   if (rc != NA3D_OK) return rc;
+  Geom g = make_geom(B, T, H, W, NH, HD, KT, KH, KW, full_box(T, H, W));
+  g.kv_span = kv_span_bytes(contiguous(T, H, W, NH, HD), H, W, HD);
   Launch l;
-  const int64_t span = kv_span_bytes(contiguous(T, H, W, NH, HD), H, W, HD);
-  rc = make_plan_config(B, T, H, W, NH, HD, KT, KH, KW, family, variant, tile_t, span, &l);
+  rc = make_plan_config(g, family, variant, tile_t, &l);
   if (rc != NA3D_OK) return rc;
   fill_plan(l, plan);
   return NA3D_OK;
@@ -447,11 +522,10 @@ int na3d_fwd(const void* q, const void* k, const void* v, void* out, int B, int 
 int na3d_fwd_config(const void* q, const void* k, const void* v, void* out, int B, int T,
                     int H, int W, int NH, int HD, int KT, int KH, int KW, int family,
                     int variant, int tile_t, void* stream) {
-  const Strides c = contiguous(T, H, W, NH, HD);
-  const long long st[20] = {c.b, c.t, c.h, c.w, c.n, c.b, c.t, c.h, c.w, c.n,
-                            c.b, c.t, c.h, c.w, c.n, c.b, c.t, c.h, c.w, c.n};
-  return na3d_fwd_strided_config(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW, st, family,
-                                 variant, tile_t, stream);
+  const Geom g = make_geom(B, T, H, W, NH, HD, KT, KH, KW, full_box(T, H, W));
+  Strides st[4];
+  contiguous_all(g, st);
+  return fwd_impl(q, k, v, out, g, st, family, variant, tile_t, stream);
 }
 
 int na3d_fwd_strided(const void* q, const void* k, const void* v, void* out, int B, int T,
@@ -465,17 +539,33 @@ int na3d_fwd_strided_config(const void* q, const void* k, const void* v, void* o
                             int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
                             const long long* strides, int family, int variant, int tile_t,
                             void* stream) {
-  int rc = na3d_check_args_strided(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW, strides);
-  if (rc != NA3D_OK) return rc;
+  if (!strides) return NA3D_ERR_NULL;
+  const Geom g = make_geom(B, T, H, W, NH, HD, KT, KH, KW, full_box(T, H, W));
   Strides st[4];
-  for (int i = 0; i < 4; ++i)
-    st[i] = Strides{strides[5 * i], strides[5 * i + 1], strides[5 * i + 2], strides[5 * i + 3],
-                    strides[5 * i + 4]};
-  Launch l;
-  rc = make_plan_config(B, T, H, W, NH, HD, KT, KH, KW, family, variant, tile_t,
-                        kv_span_bytes(st[1], H, W, HD), &l);
-  if (rc != NA3D_OK) return rc;
-  return run(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW, st, l, stream);
+  read_strides(strides, st);
+  return fwd_impl(q, k, v, out, g, st, family, variant, tile_t, stream);
+}
+
+int na3d_fwd_subgrid(const void* q, const void* k, const void* v, void* out, int B, int T,
+                     int H, int W, int NH, int HD, int KT, int KH, int KW, const int* box,
+                     const long long* strides, void* stream) {
+  return na3d_fwd_subgrid_config(q, k, v, out, B, T, H, W, NH, HD, KT, KH, KW, box, strides, 0,
+                                 0, 0, stream);
+}
+
+int na3d_fwd_subgrid_config(const void* q, const void* k, const void* v, void* out, int B,
+                            int T, int H, int W, int NH, int HD, int KT, int KH, int KW,
+                            const int* box, const long long* strides, int family, int variant,
+                            int tile_t, void* stream) {
+  if (!box) return NA3D_ERR_NULL;
+  const Geom g = make_geom(B, T, H, W, NH, HD, KT, KH, KW,
+                           Box{box[0], box[1], box[2], box[3], box[4], box[5]});
+  Strides st[4];
+  if (strides)
+    read_strides(strides, st);
+  else
+    contiguous_all(g, st);
+  return fwd_impl(q, k, v, out, g, st, family, variant, tile_t, stream);
 }
 
 }  // extern "C"

@@ -102,7 +102,7 @@ def test_oversized_grid():
 
 
 def test_status_strings():
-    for code in range(0, -11, -1):
+    for code in range(0, -12, -1):
         s = na.status_string(code)
         assert s and s != "unknown status"
     assert na.status_string(-99) == "unknown status"
