@@ -148,7 +148,19 @@ struct Launch {
   X(33, 128, 2, 8, 1, 4, 1, 4, 2, 1, 0) \
   X(34, 64, 2, 8, 1, 4, 1, 7, 1, 1, 4)  \
   X(35, 64, 4, 4, 1, 4, 1, 4, 2, 1, 4)  \
-  X(36, 64, 2, 8, 1, 4, 1, 4, 2, 1, 4)
+  X(36, 64, 2, 8, 1, 4, 1, 4, 2, 1, 4)  \
+  X(37, 64, 4, 4, 1, 4, 1, 7, 1, 1, 4)  \
+  X(38, 64, 4, 4, 2, 4, 1, 7, 1, 1, 4)  \
+  X(39, 64, 4, 4, 2, 4, 1, 4, 2, 1, 4)  \
+  X(40, 64, 2, 8, 2, 4, 1, 7, 1, 1, 4)  \
+  X(41, 64, 2, 8, 4, 4, 1, 7, 1, 1, 4)  \
+  X(42, 64, 2, 8, 2, 4, 1, 7, 1, 2, 4)  \
+  X(43, 64, 4, 4, 2, 4, 1, 7, 1, 2, 4)  \
+  X(44, 64, 4, 4, 4, 4, 1, 7, 1, 1, 4)  \
+  X(45, 64, 4, 4, 3, 4, 1, 13, 1, 1, 3) \
+  X(46, 64, 4, 4, 3, 4, 1, 13, 1, 2, 3) \
+  X(47, 128, 2, 8, 2, 4, 1, 7, 1, 2, 0) \
+  X(48, 128, 2, 8, 2, 4, 1, 7, 1, 1, 0)
 
 struct RollVariant {
   int hd, qh, qw, wh, wt, ns, nk, ng, nbuf, occ;

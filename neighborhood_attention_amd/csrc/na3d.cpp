@@ -258,9 +258,9 @@ int pick_roll(const Geom& g, Launch* l) {
   static const int p16[] = {11};
   static const int p32[] = {12};
   static const int p64_small[] = {8, 34, 21, 26, 20, 9};       // union <= 64 keys
-  static const int p64_mid[] = {35, 26, 34, 21, 20, 1, 9, 10};  // union <= 112 keys
-  static const int p64_large[] = {5, 10, 22, 6, 7, 9};     // larger windows
-  static const int p128[] = {25, 15, 14, 13, 16, 29};
+  static const int p64_mid[] = {42, 43, 40, 38, 35, 26, 34, 21, 20, 1, 9, 10};  // <= 112 keys
+  static const int p64_large[] = {5, 46, 10, 22, 6, 7, 9};  // larger windows
+  static const int p128[] = {47, 25, 15, 14, 13, 16, 29};
   static const int p256[] = {17};
   const int un28 = std::min(2 + g.KH - 1, g.H) * std::min(8 + g.KW - 1, g.W);
   const int* pref;
