@@ -447,6 +447,38 @@ na3d_fwd_roll_kernel(const RollArgs a) {
     if (r * NT + tid < total_chunks) dma16_kv(kpl, vpl, lane_ofs(), dk + r * NT * 16, buf_bytes);
   };
 
+  // The same walk by a subset of the waves: the wave of rank `rank` among
+  // `nst` staging waves moves chunks rank*64 + lane + k*nst*64.  Used with
+  // two buffers and HD >= 128, where the waves that have no query plane in
+  // flight at a key plane stage the next one while the others compute (the
+  // compute of a key plane is long enough to cover the slower issue; at
+  // smaller HD the plane then lands late and this measured slower).
+  constexpr bool kIdleStaging = NBUF == 2 && HD >= 128;
+  auto issue_stage_by = [&](int tp, int bufi, int rank, int nst) {
+    const uint16_t* kpl = kbase + (int64_t)tp * a.sk.t;
+    const uint16_t* vpl = vbase + (int64_t)tp * a.sv.t;
+    const uint32_t dk = lds_addr(smem + bufi * 2 * buf_bytes);
+    const int c_first = rank * kWave + lane;
+    const int rs = nst * (kWave / CPR);        // halo rows per round
+    const int rs_h = rs / hwd, rs_w = rs - rs_h * hwd;
+    int row = c_first / CPR;
+    const int pcs = c_first - row * CPR;
+    int rw = row % hwd;
+    uint32_t d = (uint32_t)(hh0 + row / hwd) * sh_b + (uint32_t)(hw0 + rw) * sw_b;
+    const uint32_t ds = (uint32_t)rs_h * sh_b + (uint32_t)rs_w * sw_b;
+    for (int c0 = rank * kWave; c0 < total_chunks; c0 += nst * kWave) {
+      if (c0 + lane < total_chunks)
+        dma16_kv(kpl, vpl, d + (uint32_t)((pcs ^ swz(HD, row)) << 4), dk + c0 * 16, buf_bytes);
+      d += ds;
+      row += rs;
+      rw += rs_w;
+      if (rw >= hwd) {
+        rw -= hwd;
+        d += dwrap;
+      }
+    }
+  };
+
   // zero the rows past the halo in every buffer (never staged; read only as
   // masked keys); the first barrier of the stream orders these stores
   {
@@ -490,7 +522,13 @@ na3d_fwd_roll_kernel(const RollArgs a) {
     }
     auto tq = [&](int j) { return t0 + it + WT * j; };
     int jlo = 0, jhi = -1;  // query planes j in [jlo, jhi] are in flight
+    // query planes [alo, ahi] of the run (any wave) are in flight
+    int alo = t0, ahi = t0 - 1;
     for (int tp = p0; tp < p1; ++tp, ++st) {
+      if (kIdleStaging) {
+        while (ahi + 1 < t1 && wst(ahi + 1) <= tp) ++ahi;
+        while (alo <= ahi && wst(alo) + KT - 1 < tp) ++alo;
+      }
       // admit this wave's query planes whose window starts here
       while (tq(jhi + 1) < t1 && wst(tq(jhi + 1)) <= tp) {
         ++jhi;
@@ -517,7 +555,30 @@ na3d_fwd_roll_kernel(const RollArgs a) {
         pend_on = false;
       }
       const int nxt = tp + 1 < p1 ? tp + 1 : np0;  // plane of the next step, -1 = none
-      if (NBUF == 2 && nxt >= 0) issue_stage(nxt, (st + 1) & 1);
+      if (NBUF == 2 && nxt >= 0 && !kIdleStaging) {
+        issue_stage(nxt, (st + 1) & 1);
+      } else if (NBUF == 2 && nxt >= 0) {
+        // waves with nothing to compute at this key plane stage the next one
+        // (all waves when none is idle): a wave of phase i is busy when one of
+        // the in-flight planes [alo, ahi] is congruent to t0 + i mod WT
+        const int nin = ahi - alo + 1;
+        const int ph = (alo - t0) % WT;
+        uint32_t busy_ph = nin >= WT ? (1u << WT) - 1u
+                                     : ((((1u << nin) - 1u) << ph) | (((1u << nin) - 1u) >> (WT - ph))) &
+                                           ((1u << WT) - 1u);
+        uint32_t idle = 0;
+#pragma unroll
+        for (int w = 0; w < WH * WT; ++w) {
+          const bool blk = h0 + (w % WH) * QH < Hq;
+          if (!blk || !((busy_ph >> (w / WH)) & 1u)) idle |= 1u << w;
+        }
+        if (idle == 0) {
+          issue_stage(nxt, (st + 1) & 1);
+        } else if ((idle >> wave) & 1u) {
+          issue_stage_by(nxt, (st + 1) & 1, __builtin_popcount(idle & ((1u << wave) - 1u)),
+                         __builtin_popcount(idle));
+        }
+      }
       // fetch Q of the query plane (if any) this wave admits at the next step
       {
         int tn = -1;
