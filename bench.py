@@ -359,6 +359,13 @@ def main():
             "value": lw["value"], "unit": "TFLOP/s", "mfma_peak_frac": lw["mfma_peak_frac"],
             "ms_per_step": lw["ms_per_step"], "kernel_us": lw["kernel_us"],
             "roofline": lw["roofline"], "parity_sampled": lw["parity_sampled"]}
+        # the pages' anisotropic wide-window benchmark grid, (3,5,27)
+        ww = bench_workload("wide_w27", args.steps, args.warmup, check=not args.no_check,
+                            cpu=False)
+        rec["wide_window_3x5x27"] = {
+            "shape_BTHWNH_HD": ww["config"]["shape_BTHWNH_HD"], "value": ww["value"],
+            "unit": "TFLOP/s", "kernel_us": ww["kernel_us"], "roofline": ww["roofline"],
+            "parity_sampled": ww["parity_sampled"], "variant": ww["config"]["variant"]}
     if args.workload == HEADLINE and not args.no_fused:
         rec["fused_qkv_inputs"] = bench_fused(args.workload, args.steps, args.warmup)
     if args.workload == HEADLINE and not args.no_split:

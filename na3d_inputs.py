@@ -71,6 +71,9 @@ WORKLOADS = {
         Workload("full_scale", (1, 32, 128, 192, 16, 128), (3, 7, 7), 5,
                  k_outlier_frac=0.01, k_outlier_scale=8.0,
                  note="1% of k elements x8"),
+        Workload("wide_w27", (1, 4, 8, 128, 8, 64), (3, 5, 27), 6,
+                 note="anisotropic wide window; grid of the aiter PR's (3,5,27) "
+                      "benchmark row (its head count is not stated; 8 here)"),
     )
 }
 

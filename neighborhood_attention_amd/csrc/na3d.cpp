@@ -259,7 +259,9 @@ int pick_roll(const Geom& g, Launch* l) {
   static const int p32[] = {12};
   static const int p64_small[] = {8, 34, 21, 26, 20, 9};       // union <= 64 keys
   static const int p64_mid[] = {42, 43, 40, 38, 35, 26, 34, 21, 20, 1, 9, 10};  // <= 112 keys
-  static const int p64_large[] = {5, 46, 10, 22, 6, 7, 9};  // larger windows
+  // larger windows: 4x4 blocks for near-cubic ones; 2x8 blocks for windows
+  // much wider along W (their union is smaller in 2x8 blocks)
+  static const int p64_large[] = {5, 46, 51, 50, 49, 10, 22, 6, 7, 9};
   static const int p128[] = {47, 25, 15, 14, 13, 16, 29};
   static const int p256[] = {17};
   const int un28 = std::min(2 + g.KH - 1, g.H) * std::min(8 + g.KW - 1, g.W);
