@@ -39,6 +39,10 @@ KERNEL_SOURCES = ("neighborhood_attention_amd/csrc/common.h",
                   "neighborhood_attention_amd/csrc/kernel_roll.hip",
                   "neighborhood_attention_amd/csrc/kernel_general.hip",
                   "neighborhood_attention_amd/csrc/na3d.cpp")
+NORM_SOURCES = ("neighborhood_attention_amd/csrc/common.h",
+                "neighborhood_attention_amd/csrc/kernel_rmsnorm.hip",
+                "neighborhood_attention_amd/csrc/na3d.cpp")
+NORM_EPS = 1e-6
 
 
 def parse():
@@ -58,6 +62,8 @@ def parse():
                     help="headline run without the fused-QKV input companion measurement")
     ap.add_argument("--no-split", action="store_true",
                     help="headline run without the 2x2 query-box split companion measurement")
+    ap.add_argument("--no-rms-norm", action="store_true",
+                    help="headline run without the RMSNorm block-norm companion measurement")
     ap.add_argument("--no-check", action="store_true",
                     help="skip the sampled parity check before timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -65,24 +71,24 @@ def parse():
     return ap.parse_args()
 
 
-def sources_sha256():
+def sources_sha256(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, profile="na3d_fwd_roll_%s_traffic.md", sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed counter summary of this
     workload, if it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "na3d_fwd_roll_%s_traffic.md" % workload)
+    path = os.path.join(ROOT, "profiles", profile % workload)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
     tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not sha or not tb or sha.group(1) != sources_sha256():
+    if not sha or not tb or sha.group(1) != sources_sha256(sources):
         return None
     return float(tb.group(1))
 
@@ -315,6 +321,74 @@ def bench_split(name, steps, warmup):
     }
 
 
+def bench_rms_norm(launches=400, warmup=20, check=True, cpu_s=3.0):
+    """The bf16 RMSNorm block norm on its stand-in workload (24576 tokens x
+    4096 channels, with weight): HBM-bound, so the figure is GB/s of
+    algorithmic bytes (x read once, y written once, the weight once) against
+    the 8 TB/s peak.  Parity gate first: every element of 64 random rows
+    against the oracle, within the kernel's one-rounding bound.  A launch
+    takes about 60 us, so the headline's step count is multiplied by 8."""
+    import torch
+
+    import neighborhood_attention_amd as na
+    from na3d_inputs import NORM_WORKLOADS, make_norm_inputs
+    from oracle.rmsnorm import rms_norm as oracle_rms_norm
+
+    wl = NORM_WORKLOADS["rms_block_norm"]
+    x, w = make_norm_inputs(wl.rows, wl.dim, wl.seed, "cuda")
+    y = torch.empty_like(x)
+    fn = lambda: na.rms_norm(x, w, NORM_EPS, out=y)
+    fn()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(wl.seed)
+    sample = np.sort(rng.choice(wl.rows, 64, replace=False))
+    xs = x[torch.as_tensor(sample, device=x.device)].float().cpu().numpy()
+    wn = w.float().cpu().numpy()
+    worst = None
+    if check:
+        ref = oracle_rms_norm(xs, wn, NORM_EPS)
+        got = y[torch.as_tensor(sample, device=x.device)].double().cpu().numpy()
+        ratio = np.abs(got - ref) / (np.abs(ref) + 1e-30)
+        worst = float(ratio.max())
+        if worst > 2.0 ** -8 + 2.0 ** -14:
+            raise SystemExit("parity gate failed on the RMSNorm workload: worst relative "
+                             "error %.3e" % worst)
+    _, kern_ms = time_kernel(fn, launches, warmup)
+    kern_s = kern_ms * 1e-3
+    tbytes = measured_traffic(wl.name, "rms_norm_%s_traffic.md", NORM_SOURCES)
+    gbs = wl.bytes / kern_s / 1e9
+    # CPU baseline: the oracle (numpy, one thread) on a bounded number of rows,
+    # GB/s of the same algorithmic bytes per row
+    n = 256
+    t0 = time.perf_counter()
+    oracle_rms_norm(xs.repeat(n // 64, axis=0), wn, NORM_EPS)
+    dt = time.perf_counter() - t0
+    n = int(min(wl.rows, max(n, n * cpu_s / max(dt, 1e-9))))
+    xb = np.resize(xs, (n, wl.dim))
+    t0 = time.perf_counter()
+    oracle_rms_norm(xb, wn, NORM_EPS)
+    dt = time.perf_counter() - t0
+    per_row = wl.bytes / wl.rows
+    return {
+        "workload": wl.name, "rows": wl.rows, "dim": wl.dim, "weight": True, "eps": NORM_EPS,
+        "launches": launches, "kernel_us": round(kern_ms * 1e3, 2),
+        "value": round(gbs, 1), "unit": "GB/s",
+        "roofline": {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": None if tbytes is None else round(tbytes / kern_s / 1e9, 1),
+            "traffic_bytes_per_launch": tbytes,
+        },
+        "parity_sampled": {"rows": 64, "worst_rel_err": worst},
+        "cpu_baseline": {
+            "value": round(n * per_row / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d rows (copies of 64 sampled rows) of %d, %.1f s of numpy fp64 time"
+                      % (n, wl.rows, dt),
+        },
+    }
+
+
 def copy_calibration(nbytes):
     """A plain device copy of a known size, for scaling memory counters."""
     import torch
@@ -370,6 +444,10 @@ def main():
         rec["fused_qkv_inputs"] = bench_fused(args.workload, args.steps, args.warmup)
     if args.workload == HEADLINE and not args.no_split:
         rec["query_box_split_2x2"] = bench_split(args.workload, args.steps, args.warmup)
+    if args.workload == HEADLINE and not args.no_rms_norm:
+        rec["rms_norm_block_norm"] = bench_rms_norm(8 * args.steps, 4 * args.warmup,
+                                                    check=not args.no_check,
+                                                    cpu_s=0.0 if args.no_cpu_baseline else 3.0)
     print(json.dumps(rec), flush=True)
     return 0
 

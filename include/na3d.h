@@ -47,12 +47,13 @@ extern "C" {
 #define NA3D_ERR_WINDOW (-3)   /* a window extent is < 1 or exceeds its grid axis */
 #define NA3D_ERR_HEAD_DIM (-4) /* HD is not one of 16, 32, 64, 128, 256 */
 #define NA3D_ERR_ALIGN (-5)    /* a pointer is not 16-byte aligned */
-#define NA3D_ERR_OVERLAP (-6)  /* out overlaps q, k or v */
+#define NA3D_ERR_OVERLAP (-6)  /* an output overlaps an input it must not overlap */
 #define NA3D_ERR_DEVICE (-7)   /* the current HIP device is not gfx950 */
 #define NA3D_ERR_LAUNCH (-8)   /* the kernel launch was rejected by HIP */
 #define NA3D_ERR_CONFIG (-9)   /* an explicit launch configuration cannot run the sizes */
 #define NA3D_ERR_STRIDE (-10)  /* a stride set na3d_fwd_strided cannot take (see there) */
 #define NA3D_ERR_BOX (-11)     /* a query box that is empty or reaches outside the grid */
+#define NA3D_ERR_VALUE (-12)   /* a scalar argument out of range (RMSNorm eps) */
 
 /*
  * Forward pass of 3-D neighborhood attention.
@@ -197,6 +198,46 @@ int na3d_fwd_subgrid_config(const void* q, const void* k, const void* v,
                             int HD, int KT, int KH, int KW, const int* box,
                             const long long* strides, int family, int variant,
                             int tile_t, void* stream);
+
+/*
+ * RMSNorm over the last axis, bf16 in and out: the transformer block norms
+ * of the xDiT PR "LTX-2.5 optimizations: add parallel VAE decoding and AITER
+ * RMSNorm" (Changes, item 2; a drop-in for a norm that normalises in float32,
+ * with or without an elementwise weight).  For every row r and column j,
+ *   y[r, j] = x[r, j] * w[j] / sqrt( (1/dim) * sum_k x[r, k]^2 + eps )
+ * with w = 1 when weight is NULL.  The sum of squares, the scale and both
+ * products are taken in fp32; y is rounded to bf16 once (round to nearest
+ * even).  Squares are summed in fp32, so a row whose sum of squares exceeds
+ * the fp32 range (|x| beyond about 1.8e19 / sqrt(dim)) normalises to zero.
+ *   x      : device pointer, bf16, (rows, dim) contiguous (row stride dim)
+ *   weight : device pointer, bf16, (dim,), or NULL for a unit weight
+ *   y      : device pointer, bf16, (rows, dim) contiguous; fully overwritten.
+ *            y == x (in place) is allowed; any other overlap of y with x, and
+ *            any overlap of y with weight, is NA3D_ERR_OVERLAP
+ *   rows   : >= 0; with 0 rows nothing is read or written, the call returns
+ *            NA3D_OK after the dim and eps checks, and the pointers may be NULL
+ *   dim    : a multiple of 8 in [8, 8192] (NA3D_ERR_SHAPE otherwise)
+ *   eps    : finite and >= 0 (NA3D_ERR_VALUE otherwise); with eps = 0 an
+ *            all-zero row gives NaN, as the formula does
+ *   stream : hipStream_t to enqueue on, or NULL for the default stream
+ * x, weight and y must be 16-byte aligned (NA3D_ERR_ALIGN).  Ownership,
+ * asynchrony and error reporting are as for na3d_fwd.
+ */
+int na3d_rms_norm(const void* x, const void* weight, void* y, int rows, int dim,
+                  float eps, void* stream);
+
+/* The argument checks of na3d_rms_norm alone, without touching a device. */
+int na3d_check_args_rms_norm(const void* x, const void* weight, const void* y,
+                             int rows, int dim, float eps);
+
+/*
+ * na3d_rms_norm with an explicit grid of `workgroups` workgroups of four
+ * waves (each wave normalises rows wave, wave + 4*workgroups, ...), for
+ * tuning sweeps and for testing the multi-row path; 0 = automatic,
+ * negative or above 2^24 = NA3D_ERR_CONFIG.
+ */
+int na3d_rms_norm_config(const void* x, const void* weight, void* y, int rows,
+                         int dim, float eps, int workgroups, void* stream);
 
 /* Number of rolling-family instantiations compiled into the library. */
 int na3d_num_variants(void);

@@ -17,6 +17,13 @@ N(0,1) draws of the same shapes; no model weights or dataset are involved):
 The draws are deterministic for a given (seed, device type, torch version);
 CPU and GPU streams differ, so a test generates once and copies the same
 bytes to both sides.
+
+RMSNorm inputs (the transformer block norms of the xDiT LTX-2.5 PR page,
+Changes item 2; the pages give no hidden size or token count, so a stand-in
+of 24576 tokens x 4096 channels is used): ``x = bf16(randn * exp(randn_row))``
+-- N(0,1) channels with a log-normal per-token scale, since hidden-state
+magnitudes vary from token to token -- and ``weight = bf16(1 + 0.1 * randn)``,
+a norm weight near its ones initialisation.
 """
 from __future__ import annotations
 
@@ -76,6 +83,42 @@ WORKLOADS = {
                       "benchmark row (its head count is not stated; 8 here)"),
     )
 }
+
+
+@dataclass(frozen=True)
+class NormWorkload:
+    name: str
+    rows: int
+    dim: int
+    seed: int
+    note: str = field(default="", compare=False)
+
+    @property
+    def bytes(self) -> int:
+        """Compulsory HBM bytes: x read once, y written once, the weight read once."""
+        return 2 * self.rows * self.dim * 2 + self.dim * 2
+
+
+NORM_WORKLOADS = {
+    w.name: w
+    for w in (
+        NormWorkload("rms_tiny", 37, 520, 20, note="ragged: 65 16-byte pieces per row"),
+        NormWorkload("rms_block_norm", 24576, 4096, 21,
+                     note="stand-in for one block norm over a video latent: 24576 tokens "
+                          "(16 x 32 x 48) x 4096 channels"),
+    )
+}
+
+
+def make_norm_inputs(rows: int, dim: int, seed: int, device="cpu"):
+    """Draw (x, weight): x (rows, dim) and weight (dim,), contiguous bf16."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed))
+    scale = torch.exp(torch.randn((rows, 1), generator=g, device=dev))
+    x = (torch.randn((rows, dim), generator=g, device=dev) * scale).to(torch.bfloat16)
+    w = (1.0 + 0.1 * torch.randn((dim,), generator=g, device=dev)).to(torch.bfloat16)
+    return x, w
 
 
 def make_inputs(shape, seed: int, device="cpu", k_outlier_frac: float = 0.0,

@@ -32,11 +32,13 @@ NA3D_ERR_LAUNCH = -8
 NA3D_ERR_CONFIG = -9
 NA3D_ERR_STRIDE = -10
 NA3D_ERR_BOX = -11
+NA3D_ERR_VALUE = -12
 
 EXPORTS = ("na3d_fwd", "na3d_check_args", "na3d_status_string", "na3d_plan",
            "na3d_fwd_config", "na3d_plan_config", "na3d_fwd_strided", "na3d_check_args_strided",
            "na3d_fwd_strided_config", "na3d_fwd_subgrid", "na3d_check_args_subgrid",
-           "na3d_fwd_subgrid_config", "na3d_num_variants", "na3d_abi_version")
+           "na3d_fwd_subgrid_config", "na3d_rms_norm", "na3d_check_args_rms_norm",
+           "na3d_rms_norm_config", "na3d_num_variants", "na3d_abi_version")
 PLAN_KEYS = ("family", "tile_t", "tile_h", "tile_w", "workgroups", "threads", "lds_bytes",
              "planes", "variant", "runs")
 
@@ -87,6 +89,13 @@ def load(path: str = LIB_PATH):
         lib.na3d_check_args_subgrid.restype = i32
         lib.na3d_fwd_subgrid_config.argtypes = [p, p, p, p] + [i32] * 9 + [ip, ll] + [i32] * 3 + [p]
         lib.na3d_fwd_subgrid_config.restype = i32
+        f32 = ctypes.c_float
+        lib.na3d_rms_norm.argtypes = [p, p, p, i32, i32, f32, p]
+        lib.na3d_rms_norm.restype = i32
+        lib.na3d_check_args_rms_norm.argtypes = [p, p, p, i32, i32, f32]
+        lib.na3d_check_args_rms_norm.restype = i32
+        lib.na3d_rms_norm_config.argtypes = [p, p, p, i32, i32, f32, i32, p]
+        lib.na3d_rms_norm_config.restype = i32
         lib.na3d_num_variants.argtypes = []
         lib.na3d_num_variants.restype = i32
         lib.na3d_abi_version.argtypes = []
@@ -268,4 +277,58 @@ def fwd_subgrid(q, k, v, kernel_size, offset, out=None, config=None):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), k.shape,
                 kernel_size, stream, config, strides, box)
+    return out
+
+
+def check_args_rms_norm(x_ptr, w_ptr, y_ptr, rows, dim, eps) -> int:
+    """Host-only argument check of na3d_rms_norm (no device access)."""
+    return load().na3d_check_args_rms_norm(x_ptr, w_ptr, y_ptr, int(rows), int(dim), float(eps))
+
+
+def rms_norm_raw(x_ptr: int, w_ptr, y_ptr: int, rows: int, dim: int, eps: float,
+                 stream: int = 0, workgroups=None) -> None:
+    """Call na3d_rms_norm (na3d_rms_norm_config when ``workgroups`` is given)
+    on raw device addresses; ``w_ptr`` None or 0 means a unit weight."""
+    w_ptr = w_ptr or None
+    if workgroups is None:
+        rc = load().na3d_rms_norm(x_ptr, w_ptr, y_ptr, int(rows), int(dim), float(eps), stream)
+    else:
+        rc = load().na3d_rms_norm_config(x_ptr, w_ptr, y_ptr, int(rows), int(dim), float(eps),
+                                         int(workgroups), stream)
+    if rc != NA3D_OK:
+        raise NA3DError(rc, "na3d_rms_norm")
+
+
+def rms_norm(x, weight=None, eps: float = 1e-6, out=None, workgroups=None):
+    """RMSNorm over the last axis of a contiguous bf16 GPU tensor:
+    x * weight / sqrt(mean(x**2, -1) + eps), fp32 inside, one bf16 rounding.
+
+    The drop-in block norm of the xDiT PR "LTX-2.5 optimizations: add
+    parallel VAE decoding and AITER RMSNorm" (Changes, item 2): ``weight``
+    (shape (dim,), bf16) or None for a norm without an elementwise weight.
+    ``out`` may be ``x`` itself (in place).  Enqueued on torch's current
+    stream.  ``workgroups`` forces the grid size (tuning/testing).
+    """
+    import torch
+
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.device.type != "cuda":
+        raise TypeError("x must be a bfloat16 GPU tensor")
+    if x.dim() < 1 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous tensor with at least one axis")
+    dim = x.shape[-1]
+    rows = x.numel() // dim if dim else 0
+    if weight is not None:
+        if (not isinstance(weight, torch.Tensor) or weight.dtype != torch.bfloat16
+                or weight.device != x.device or tuple(weight.shape) != (dim,)
+                or not weight.is_contiguous()):
+            raise ValueError("weight must be a contiguous bf16 (dim,) tensor on x's device")
+    if out is None:
+        out = torch.empty_like(x)
+    elif (out.shape != x.shape or out.dtype != torch.bfloat16 or out.device != x.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous bf16 tensor shaped like x")
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rms_norm_raw(x.data_ptr(), None if weight is None else weight.data_ptr(),
+                     out.data_ptr(), rows, dim, eps, stream, workgroups)
     return out

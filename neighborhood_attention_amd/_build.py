@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", f)
-           for f in ("na3d.cpp", "kernel_general.hip", "kernel_roll.hip")]
+           for f in ("na3d.cpp", "kernel_general.hip", "kernel_roll.hip", "kernel_rmsnorm.hip")]
 LIB = os.path.join(HERE, "libna3d.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

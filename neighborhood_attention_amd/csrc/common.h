@@ -180,4 +180,11 @@ constexpr int kNumRollVariants = sizeof(kRollVariants) / sizeof(kRollVariants[0]
 int launch_general(const Problem& p, const Launch& l, int hd, hipStream_t s);
 int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s);
 
+// RMSNorm (kernel_rmsnorm.hip): 16-byte pieces held per lane for a row of
+// `dim` bf16, and the launch (wgs = 0: automatic grid; 0 on success).
+constexpr int kRmsMaxDim = 8192;
+int rms_norm_pieces_per_lane(int dim);
+int launch_rms_norm(const void* x, const void* w, void* y, int rows, int dim, float eps, int wgs,
+                    hipStream_t s);
+
 }  // namespace na3d

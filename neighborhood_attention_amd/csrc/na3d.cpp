@@ -433,6 +433,37 @@ void fill_plan(const Launch& l, int* plan) {
   plan[9] = l.tiles_t;
 }
 
+// Argument contract of the RMSNorm entry points.
+int rms_check(const void* x, const void* w, const void* y, int rows, int dim, float eps) {
+  if (rows < 0 || dim < 8 || dim % 8 != 0 || dim > kRmsMaxDim) return NA3D_ERR_SHAPE;
+  // bit test behind an opaque barrier: the library is built without NaN
+  // semantics, so a float test (or a bit test the compiler can see through)
+  // could be folded into an infinity-only check
+  uint32_t eb;
+  std::memcpy(&eb, &eps, 4);
+  asm volatile("" : "+r"(eb));
+  if ((eb & 0x7f800000u) == 0x7f800000u || eps < 0.f) return NA3D_ERR_VALUE;
+  if (rows == 0) return NA3D_OK;  // nothing is read or written
+  if (!x || !y) return NA3D_ERR_NULL;
+  if (((uintptr_t)x | (uintptr_t)y | (uintptr_t)w) & 15) return NA3D_ERR_ALIGN;
+  const size_t n = (size_t)rows * dim * 2;
+  if (x != y && overlaps2(y, n, x, n)) return NA3D_ERR_OVERLAP;
+  if (w && overlaps2(y, n, w, (size_t)dim * 2)) return NA3D_ERR_OVERLAP;
+  return NA3D_OK;
+}
+
+int rms_impl(const void* x, const void* w, void* y, int rows, int dim, float eps, int wgs,
+             void* stream) {
+  int rc = rms_check(x, w, y, rows, dim, eps);
+  if (rc != NA3D_OK) return rc;
+  if (wgs < 0 || wgs > (1 << 24)) return NA3D_ERR_CONFIG;
+  if (rows == 0) return NA3D_OK;
+  rc = device_ok();
+  if (rc != NA3D_OK) return rc;
+  rc = launch_rms_norm(x, w, y, rows, dim, eps, wgs, static_cast<hipStream_t>(stream));
+  return rc == 0 ? NA3D_OK : NA3D_ERR_LAUNCH;
+}
+
 
 
 }  // namespace
@@ -454,7 +485,7 @@ const char* na3d_status_string(int status) {
     case NA3D_ERR_WINDOW: return "a window extent is < 1 or larger than its grid axis";
     case NA3D_ERR_HEAD_DIM: return "head dimension must be 16, 32, 64, 128 or 256";
     case NA3D_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-    case NA3D_ERR_OVERLAP: return "out overlaps q, k or v";
+    case NA3D_ERR_OVERLAP: return "an output overlaps an input it must not overlap";
     case NA3D_ERR_DEVICE: return "the current HIP device is not gfx950";
     case NA3D_ERR_LAUNCH: return "the kernel launch failed";
     case NA3D_ERR_CONFIG: return "the requested launch configuration cannot run these sizes";
@@ -462,6 +493,7 @@ const char* na3d_status_string(int status) {
       return "a stride is negative or not a multiple of 8, k and v differ in H/W/NH strides, "
              "or out's strides map two elements to one address";
     case NA3D_ERR_BOX: return "the query box is empty or reaches outside the grid";
+    case NA3D_ERR_VALUE: return "eps is negative or not finite";
     default: return "unknown status";
   }
 }
@@ -568,6 +600,21 @@ int na3d_fwd_subgrid_config(const void* q, const void* k, const void* v, void* o
   else
     contiguous_all(g, st);
   return fwd_impl(q, k, v, out, g, st, family, variant, tile_t, stream);
+}
+
+int na3d_check_args_rms_norm(const void* x, const void* weight, const void* y, int rows,
+                             int dim, float eps) {
+  return rms_check(x, weight, y, rows, dim, eps);
+}
+
+int na3d_rms_norm(const void* x, const void* weight, void* y, int rows, int dim, float eps,
+                  void* stream) {
+  return rms_impl(x, weight, y, rows, dim, eps, 0, stream);
+}
+
+int na3d_rms_norm_config(const void* x, const void* weight, void* y, int rows, int dim,
+                         float eps, int workgroups, void* stream) {
+  return rms_impl(x, weight, y, rows, dim, eps, workgroups, stream);
 }
 
 }  // extern "C"
