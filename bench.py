@@ -62,6 +62,8 @@ def parse():
                     help="headline run without the fused-QKV input companion measurement")
     ap.add_argument("--no-split", action="store_true",
                     help="headline run without the 2x2 query-box split companion measurement")
+    ap.add_argument("--no-batch", action="store_true",
+                    help="headline run without the batched decoder-tiles companion measurement")
     ap.add_argument("--no-rms-norm", action="store_true",
                     help="headline run without the RMSNorm block-norm companion measurement")
     ap.add_argument("--no-check", action="store_true",
@@ -389,6 +391,47 @@ def bench_rms_norm(launches=400, warmup=20, check=True, cpu_s=3.0):
     }
 
 
+def bench_batch(steps, warmup):
+    """A corner of a decoder tile grid, 2 x 3 tiles with narrow right and
+    bottom edges ((16,64,96) x 2, (16,64,7) x 2, (16,32,96), (16,32,7); NH=8,
+    HD=64, window 3x7x7), run as one batch (na3d_fwd_batch: one launch)
+    against one na3d_fwd launch per tile back to back.  Every batched output
+    is first checked bitwise against the same tile run alone with the
+    batch's instantiation."""
+    import torch
+
+    import neighborhood_attention_amd as na
+    from na3d_inputs import make_inputs
+
+    NH, HD, ks = 8, 64, (3, 7, 7)
+    dims = [(1, 16, 64, 96)] * 2 + [(1, 16, 64, 7)] * 2 + [(1, 16, 32, 96), (1, 16, 32, 7)]
+    qkv = [make_inputs(d + (NH, HD), 40 + i, "cuda") for i, d in enumerate(dims)]
+    outs = [torch.empty_like(t[0]) for t in qkv]
+    plan = na.plan_batch(dims, NH, HD, ks)
+    na.fwd_batch(qkv, ks, outs=outs)
+    for (q, k, v), o in zip(qkv, outs):
+        if not torch.equal(o, na.fwd(q, k, v, ks, config=(2, plan["variant"], 0))):
+            raise SystemExit("batched tile differs from the same tile run alone")
+    torch.cuda.synchronize()
+    solo = [torch.empty_like(t[0]) for t in qkv]
+
+    def separate():
+        for (q, k, v), o in zip(qkv, solo):
+            na.fwd(q, k, v, ks, out=o)
+
+    _, batch_ms = time_kernel(lambda: na.fwd_batch(qkv, ks, outs=outs), steps, warmup)
+    _, sep_ms = time_kernel(separate, steps, warmup)
+    flops = sum(4 * d[0] * d[1] * d[2] * d[3] * NH * ks[0] * ks[1] * ks[2] * HD for d in dims)
+    return {
+        "tiles": [list(d) for d in dims], "NH": NH, "HD": HD, "window": list(ks),
+        "launches": plan["launches"], "variant": plan["variant"],
+        "kernel_us_batched": round(batch_ms * 1e3, 2),
+        "kernel_us_one_launch_per_tile": round(sep_ms * 1e3, 2),
+        "value": round(flops / (batch_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "bitwise_equal_to_tiles_alone": True,
+    }
+
+
 def copy_calibration(nbytes):
     """A plain device copy of a known size, for scaling memory counters."""
     import torch
@@ -444,6 +487,8 @@ def main():
         rec["fused_qkv_inputs"] = bench_fused(args.workload, args.steps, args.warmup)
     if args.workload == HEADLINE and not args.no_split:
         rec["query_box_split_2x2"] = bench_split(args.workload, args.steps, args.warmup)
+    if args.workload == HEADLINE and not args.no_batch:
+        rec["decoder_tiles_batched"] = bench_batch(args.steps, args.warmup)
     if args.workload == HEADLINE and not args.no_rms_norm:
         rec["rms_norm_block_norm"] = bench_rms_norm(8 * args.steps, 4 * args.warmup,
                                                     check=not args.no_check,

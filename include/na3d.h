@@ -200,6 +200,53 @@ int na3d_fwd_subgrid_config(const void* q, const void* k, const void* v,
                             int tile_t, void* stream);
 
 /*
+ * One tile of a batch: q, k, v and out are contiguous bf16 (B, T, H, W, NH,
+ * HD) device tensors of this tile, with the NH, HD and window of the batch.
+ */
+typedef struct na3d_tile {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int B, T, H, W;
+} na3d_tile;
+
+/*
+ * na3d_fwd on many independent grids at once: the video decoder runs NA3D on
+ * every tile of a tile grid, and its edge tiles are narrow (xDiT PR 773 page
+ * "LTX-2.5 optimization: integrate faster AITER NA3D flash attention for
+ * diffusion decoder", Summary; xDiT PR 759 page, Changes item 1: each tile's
+ * decode is independent of the others).  out of every tile is bitwise what
+ * na3d_fwd_config writes for that tile alone with the launch's rolling
+ * instantiation (see na3d_plan_batch), and within rounding of na3d_fwd.
+ *   tiles : host array of n descriptors, read during the call only
+ *   n     : >= 0 (0 returns NA3D_OK without touching the device)
+ *   NH, HD, KT, KH, KW : shared by every tile, as for na3d_fwd (the window
+ *           must fit each tile's grid)
+ * Tiles that the rolling instantiation chosen for the largest tile can run
+ * share kernel launches, up to 16 tiles each, in the given order; any other
+ * tile is run by a launch of its own.  All launches are enqueued on
+ * `stream` in order.  Each tile must pass na3d_fwd's checks, and no tile's
+ * out may overlap any tensor of another tile (NA3D_ERR_OVERLAP); inputs may
+ * be shared between tiles.  Errors are detected before any launch.
+ */
+int na3d_fwd_batch(const na3d_tile* tiles, int n, int NH, int HD, int KT,
+                   int KH, int KW, void* stream);
+
+/* The argument checks of na3d_fwd_batch alone, without touching a device. */
+int na3d_check_args_batch(const na3d_tile* tiles, int n, int NH, int HD,
+                          int KT, int KH, int KW);
+
+/*
+ * How na3d_fwd_batch would run a batch (only the tiles' sizes are read):
+ * plan[0] = kernel launches, plan[1] = rolling instantiation of the shared
+ * launches (-1 if none), plan[2] = tiles in shared launches, plan[3] =
+ * workgroups of the first shared launch.  `plan` must hold 4 ints.
+ */
+int na3d_plan_batch(const na3d_tile* tiles, int n, int NH, int HD, int KT,
+                    int KH, int KW, int* plan);
+
+/*
  * RMSNorm over the last axis, bf16 in and out: the transformer block norms
  * of the xDiT PR "LTX-2.5 optimizations: add parallel VAE decoding and AITER
  * RMSNorm" (Changes, item 2; a drop-in for a norm that normalises in float32,

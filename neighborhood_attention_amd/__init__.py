@@ -38,12 +38,20 @@ EXPORTS = ("na3d_fwd", "na3d_check_args", "na3d_status_string", "na3d_plan",
            "na3d_fwd_config", "na3d_plan_config", "na3d_fwd_strided", "na3d_check_args_strided",
            "na3d_fwd_strided_config", "na3d_fwd_subgrid", "na3d_check_args_subgrid",
            "na3d_fwd_subgrid_config", "na3d_rms_norm", "na3d_check_args_rms_norm",
-           "na3d_rms_norm_config", "na3d_num_variants", "na3d_abi_version")
+           "na3d_rms_norm_config", "na3d_fwd_batch", "na3d_check_args_batch",
+           "na3d_plan_batch", "na3d_num_variants", "na3d_abi_version")
 PLAN_KEYS = ("family", "tile_t", "tile_h", "tile_w", "workgroups", "threads", "lds_bytes",
              "planes", "variant", "runs")
 
 _lock = threading.Lock()
 _lib = None
+
+
+class Tile(ctypes.Structure):
+    """``na3d_tile``: one grid of a batch (device addresses and sizes)."""
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("B", ctypes.c_int), ("T", ctypes.c_int),
+                ("H", ctypes.c_int), ("W", ctypes.c_int)]
 
 
 class NA3DError(RuntimeError):
@@ -96,6 +104,13 @@ def load(path: str = LIB_PATH):
         lib.na3d_check_args_rms_norm.restype = i32
         lib.na3d_rms_norm_config.argtypes = [p, p, p, i32, i32, f32, i32, p]
         lib.na3d_rms_norm_config.restype = i32
+        tp = ctypes.POINTER(Tile)
+        lib.na3d_fwd_batch.argtypes = [tp, i32] + [i32] * 5 + [p]
+        lib.na3d_fwd_batch.restype = i32
+        lib.na3d_check_args_batch.argtypes = [tp, i32] + [i32] * 5
+        lib.na3d_check_args_batch.restype = i32
+        lib.na3d_plan_batch.argtypes = [tp, i32] + [i32] * 5 + [ctypes.POINTER(i32)]
+        lib.na3d_plan_batch.restype = i32
         lib.na3d_num_variants.argtypes = []
         lib.na3d_num_variants.restype = i32
         lib.na3d_abi_version.argtypes = []
@@ -332,3 +347,81 @@ def rms_norm(x, weight=None, eps: float = 1e-6, out=None, workgroups=None):
         rms_norm_raw(x.data_ptr(), None if weight is None else weight.data_ptr(),
                      out.data_ptr(), rows, dim, eps, stream, workgroups)
     return out
+
+
+def _tile_array(tiles):
+    """tiles: sequence of (q_ptr, k_ptr, v_ptr, out_ptr, (B, T, H, W))."""
+    arr = (Tile * max(len(tiles), 1))()
+    for i, (q, k, v, o, dims) in enumerate(tiles):
+        B, T, H, W = (int(x) for x in dims)
+        arr[i] = Tile(q, k, v, o, B, T, H, W)
+    return arr
+
+
+def check_args_batch(tiles, NH, HD, kernel_size) -> int:
+    """Host-only check of a batch given as (q_ptr, k_ptr, v_ptr, out_ptr,
+    (B, T, H, W)) tuples (no device access)."""
+    KT, KH, KW = (int(x) for x in kernel_size)
+    return load().na3d_check_args_batch(_tile_array(tiles), len(tiles), int(NH), int(HD),
+                                        KT, KH, KW)
+
+
+def plan_batch(dims, NH, HD, kernel_size) -> dict:
+    """How a batch of grids of the given (B, T, H, W) sizes would be launched."""
+    KT, KH, KW = (int(x) for x in kernel_size)
+    arr = _tile_array([(0, 0, 0, 0, d) for d in dims])
+    buf = (ctypes.c_int * 4)()
+    rc = load().na3d_plan_batch(arr, len(dims), int(NH), int(HD), KT, KH, KW, buf)
+    if rc != NA3D_OK:
+        raise NA3DError(rc, "na3d_plan_batch")
+    return dict(zip(("launches", "variant", "shared_tiles", "workgroups"), list(buf)))
+
+
+def fwd_batch_raw(tiles, NH, HD, kernel_size, stream: int = 0) -> None:
+    KT, KH, KW = (int(x) for x in kernel_size)
+    rc = load().na3d_fwd_batch(_tile_array(tiles), len(tiles), int(NH), int(HD), KT, KH, KW,
+                               stream)
+    if rc != NA3D_OK:
+        raise NA3DError(rc, "na3d_fwd_batch")
+
+
+def fwd_batch(qkv, kernel_size, outs=None):
+    """NA3D forward on many independent grids (e.g. the tiles of a decoder's
+    tile grid) in as few launches as possible.
+
+    qkv: sequence of (q, k, v) triples of contiguous (B,T,H,W,NH,HD) bf16 GPU
+    tensors; every triple may have its own B, T, H, W; NH, HD and the window
+    are shared.  Returns the list of outputs (new tensors unless ``outs`` is
+    given); each equals ``fwd`` on its triple alone.
+    """
+    import torch
+
+    qkv = list(qkv)
+    if not qkv:
+        return []
+    dev = qkv[0][0].device
+    NH, HD = qkv[0][0].shape[4], qkv[0][0].shape[5]
+    for i, trip in enumerate(qkv):
+        if len(trip) != 3:
+            raise ValueError("entry %d is not a (q, k, v) triple" % i)
+        for t in trip:
+            if (not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.device != dev
+                    or t.dim() != 6 or not t.is_contiguous()):
+                raise ValueError("entry %d: q, k, v must be contiguous 6-d bf16 tensors on %s"
+                                 % (i, dev))
+        if not (trip[0].shape == trip[1].shape == trip[2].shape):
+            raise ValueError("entry %d: q, k, v shapes differ" % i)
+        if trip[0].shape[4] != NH or trip[0].shape[5] != HD:
+            raise ValueError("entry %d: every tile must have NH=%d and HD=%d" % (i, NH, HD))
+    if outs is None:
+        outs = [torch.empty_like(trip[0]) for trip in qkv]
+    elif len(outs) != len(qkv) or any(
+            o.shape != t[0].shape or o.dtype != torch.bfloat16 or o.device != dev
+            or not o.is_contiguous() for o, t in zip(outs, qkv)):
+        raise ValueError("outs must be contiguous bf16 tensors shaped like each q")
+    tiles = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), q.shape[:4])
+             for (q, k, v), o in zip(qkv, outs)]
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        fwd_batch_raw(tiles, NH, HD, kernel_size, stream)
+    return outs

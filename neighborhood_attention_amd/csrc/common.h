@@ -177,8 +177,32 @@ constexpr RollVariant kRollVariants[] = {
 };
 constexpr int kNumRollVariants = sizeof(kRollVariants) / sizeof(kRollVariants[0]);
 
+// One tile of a batched rolling launch: contiguous (B,T,H,W,NH,HD) tensors,
+// every query of the grid, and the tile's own run layout.
+struct BatchTile {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int B, T, H, W;
+  int wg_off;  // the tile's first workgroup in the launch
+  int tiles_t, tiles_h, tiles_w;
+  int tc, ta, tz, nruns, rpw;
+  int lds_rows;  // the tile's own buffer rows (the launch allocates the largest)
+};
+
+constexpr int kMaxBatch = 16;  // tiles per launch (kernel arguments stay < 2 KiB)
+
+struct RollBatch {
+  int n;
+  BatchTile t[kMaxBatch];
+};
+
 int launch_general(const Problem& p, const Launch& l, int hd, hipStream_t s);
 int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s);
+// p supplies NH and the window; l the variant, grid, threads and LDS size
+int launch_roll_batch(const Problem& p, const Launch& l, const RollBatch& bt, int hd,
+                      hipStream_t s);
 
 // RMSNorm (kernel_rmsnorm.hip): 16-byte pieces held per lane for a row of
 // `dim` bf16, and the launch (wgs = 0: automatic grid; 0 on success).

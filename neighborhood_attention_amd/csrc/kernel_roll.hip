@@ -229,9 +229,10 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
 }
 
+// The whole kernel for workgroup `wg` of the problem in `a` (one grid, or
+// one tile of a batch).
 template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
-__global__ void __launch_bounds__(kWave * WH * WT) __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1)))
-na3d_fwd_roll_kernel(const RollArgs a) {
+__device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   static_assert(QH * QW == 16, "a wave owns 16 queries");
   static_assert(NBUF == 1 || NBUF == 2, "one or two plane buffers");
   constexpr int KSTEPS = Slot<HD>::KSTEPS;
@@ -264,7 +265,6 @@ na3d_fwd_roll_kernel(const RollArgs a) {
   const int it = wave / WH;
 
   // ---- workgroup -> (b, n, tile_h, tile_w, run group); run groups vary fastest
-  int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int tt = wg % a.tiles_t;
   wg /= a.tiles_t;
   const int tw = wg % a.tiles_w;
@@ -740,15 +740,66 @@ na3d_fwd_roll_kernel(const RollArgs a) {
   if (pend_on && qvalid) store_out<MT>(pend_p, pend, g);
 }
 
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
+__global__ void __launch_bounds__(kWave * WH * WT) __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1)))
+na3d_fwd_roll_kernel(const RollArgs a) {
+  roll_body<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>(a, xcd_remap(blockIdx.x, gridDim.x));
+}
+
+// Many grids in one launch: the launch's workgroups are the tiles' grids one
+// after another; a workgroup finds its tile (the last whose first workgroup
+// is not after it) and runs that tile's problem exactly as a launch of that
+// tile alone would (same staging layout, so the same arithmetic), with the
+// window and heads shared by all tiles and LDS sized for the largest.
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
+__global__ void __launch_bounds__(kWave * WH * WT) __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1)))
+na3d_fwd_roll_batch_kernel(const RollArgs shared, const RollBatch bt) {
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  int i = 0;
+  while (i + 1 < bt.n && bt.t[i + 1].wg_off <= wg) ++i;
+  const BatchTile& t = bt.t[i];
+  RollArgs a = shared;
+  a.q = t.q; a.k = t.k; a.v = t.v; a.o = t.o;
+  a.B = t.B; a.T = t.T; a.H = t.H; a.W = t.W;
+  a.t_off = 0; a.h_off = 0; a.w_off = 0;
+  a.Tq = t.T; a.Hq = t.H; a.Wq = t.W;
+  a.tiles_t = t.tiles_t; a.tiles_h = t.tiles_h; a.tiles_w = t.tiles_w;
+  a.tc = t.tc; a.ta = t.ta; a.tz = t.tz; a.nruns = t.nruns; a.rpw = t.rpw;
+  a.lds_rows = t.lds_rows;
+  Strides c;
+  c.n = HD;
+  c.w = (int64_t)a.NH * HD;
+  c.h = (int64_t)t.W * c.w;
+  c.t = (int64_t)t.H * c.h;
+  c.b = (int64_t)t.T * c.t;
+  a.sq = a.sk = a.sv = a.so = c;
+  roll_body<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>(a, wg - t.wg_off);
+}
+
 // ------------------------------------------------------------------ launch
+template <class K>
+int set_lds(K kern, int lds_bytes) {
+  return lds_bytes > 64 * 1024 &&
+                 hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     lds_bytes) != hipSuccess
+             ? -1
+             : 0;
+}
+
 template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
 int launch_cfg(const RollArgs& a, const Launch& l, hipStream_t stream) {
   auto kern = na3d_fwd_roll_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>;
-  if (l.lds_bytes > 64 * 1024 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, l.lds_bytes) != hipSuccess)
-    return -1;
+  if (set_lds(kern, l.lds_bytes) != 0) return -1;
   hipLaunchKernelGGL(kern, dim3((unsigned)l.wgs), dim3(l.threads), l.lds_bytes, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
+int launch_batch_cfg(const RollArgs& a, const RollBatch& bt, const Launch& l, hipStream_t stream) {
+  auto kern = na3d_fwd_roll_batch_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>;
+  if (set_lds(kern, l.lds_bytes) != 0) return -1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)l.wgs), dim3(l.threads), l.lds_bytes, stream, a, bt);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -780,6 +831,31 @@ int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s) {
   case i: return launch_cfg<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>(a, l, s);
     NA3D_ROLL_VARIANTS(NA3D_ROLL_CASE)
 #undef NA3D_ROLL_CASE
+    default: return -1;
+  }
+}
+
+int launch_roll_batch(const Problem& p, const Launch& l, const RollBatch& bt, int hd,
+                      hipStream_t s) {
+  RollArgs a;
+  a.q = a.k = a.v = nullptr;
+  a.o = nullptr;
+  a.B = a.T = a.H = a.W = 0;
+  a.NH = p.NH;
+  a.t_off = a.h_off = a.w_off = 0;
+  a.Tq = a.Hq = a.Wq = 0;
+  a.KT = p.KT; a.KH = p.KH; a.KW = p.KW;
+  a.tiles_t = a.tiles_h = a.tiles_w = 0;
+  a.tc = a.ta = a.tz = a.nruns = a.rpw = 0;
+  a.lds_rows = l.lds_rows;
+  a.sq = a.sk = a.sv = a.so = Strides{0, 0, 0, 0, 0};
+  if (l.variant < 0 || l.variant >= kNumRollVariants || kRollVariants[l.variant].hd != hd) return -1;
+  if (bt.n < 1 || bt.n > kMaxBatch) return -1;
+  switch (l.variant) {
+#define NA3D_ROLL_BATCH_CASE(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC) \
+  case i: return launch_batch_cfg<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>(a, bt, l, s);
+    NA3D_ROLL_VARIANTS(NA3D_ROLL_BATCH_CASE)
+#undef NA3D_ROLL_BATCH_CASE
     default: return -1;
   }
 }

@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "../../include/na3d.h"
 #include "common.h"
@@ -190,8 +191,10 @@ bool plan_general(const Geom& g, Launch* l) {
   return l->wgs <= 0x7fffffff;
 }
 
-// Can rolling variant v run these sizes?  tile_t = 0 picks the run length.
-bool plan_roll(int v, const Geom& g, int tile_t, Launch* l) {
+// Can rolling variant v run these sizes?  tile_t = 0 picks the run length;
+// `target` is the number of workgroups the launch should reach (runs are
+// shortened, and fewer runs given to one workgroup, until it does).
+bool plan_roll(int v, const Geom& g, int tile_t, Launch* l, int target = kTargetWorkgroups) {
   if (v < 0 || v >= kNumRollVariants) return false;
   const RollVariant& rv = kRollVariants[v];
   const int HD = g.HD, KH = g.KH, KW = g.KW, H = g.H, W = g.W;
@@ -216,7 +219,7 @@ bool plan_roll(int v, const Geom& g, int tile_t, Launch* l) {
   if (!choose_runs(ax, rv.wt, rv.ns, tile_t, &r)) return false;
   if (tile_t <= 0) {
     // shorter middle runs while the grid is too small to fill the chip
-    while (r.tc > rv.wt && spatial * run_count(ax, r) < kTargetWorkgroups) {
+    while (r.tc > rv.wt && spatial * run_count(ax, r) < target) {
       Runs s = r;
       s.tc = ceil_div(r.tc, 2);
       if (max_active_per_wave(ax, s, rv.wt) > rv.ns) break;
@@ -229,7 +232,7 @@ bool plan_roll(int v, const Geom& g, int tile_t, Launch* l) {
   // run's first plane is fetched during the last plane of the previous one)
   // as long as the grid keeps enough workgroups
   const int nruns = run_count(ax, r);
-  const int groups = (int)std::min<int64_t>(nruns, std::max<int64_t>(1, (kTargetWorkgroups + spatial - 1) / spatial));
+  const int groups = (int)std::min<int64_t>(nruns, std::max<int64_t>(1, (target + spatial - 1) / spatial));
   const int rpw = ceil_div(nruns, groups);
   l->family = 2;
   l->variant = v;
@@ -452,6 +455,156 @@ int rms_check(const void* x, const void* w, const void* y, int rows, int dim, fl
   return NA3D_OK;
 }
 
+// ---- batches of tiles (one launch for many grids)
+
+int64_t tile_bytes(const na3d_tile& t, int NH, int HD) {
+  return 2 * (int64_t)t.B * t.T * t.H * t.W * NH * HD;
+}
+
+Geom tile_geom(const na3d_tile& t, int NH, int HD, int KT, int KH, int KW) {
+  Geom g = make_geom(t.B, t.T, t.H, t.W, NH, HD, KT, KH, KW, full_box(t.T, t.H, t.W));
+  return g;
+}
+
+int check_batch(const na3d_tile* tiles, int n, int NH, int HD, int KT, int KH, int KW) {
+  if (n < 0) return NA3D_ERR_SHAPE;
+  if (n == 0) return NA3D_OK;
+  if (!tiles) return NA3D_ERR_NULL;
+  for (int i = 0; i < n; ++i) {
+    const na3d_tile& t = tiles[i];
+    const Geom g = tile_geom(t, NH, HD, KT, KH, KW);
+    Strides st[4];
+    contiguous_all(g, st);
+    const int rc = check_all(t.q, t.k, t.v, t.out, g, st);
+    if (rc != NA3D_OK) return rc;
+  }
+  // every output is disjoint from every other tile's tensors
+  for (int i = 0; i < n; ++i) {
+    const size_t bi = (size_t)tile_bytes(tiles[i], NH, HD);
+    for (int j = 0; j < n; ++j) {
+      if (j == i) continue;
+      const na3d_tile& u = tiles[j];
+      const size_t bj = (size_t)tile_bytes(u, NH, HD);
+      if (overlaps2(tiles[i].out, bi, u.q, bj) || overlaps2(tiles[i].out, bi, u.k, bj) ||
+          overlaps2(tiles[i].out, bi, u.v, bj) || overlaps2(tiles[i].out, bi, u.out, bj))
+        return NA3D_ERR_OVERLAP;
+    }
+  }
+  return NA3D_OK;
+}
+
+// The launches a batch takes: tiles that the rolling instantiation of the
+// largest tile can run share launches of up to kMaxBatch tiles (in the
+// given order); the others get a launch of their own with their own plan.
+struct BatchPlan {
+  int variant = -1;                 // rolling instantiation of the shared launches
+  std::vector<Launch> plan;         // per tile
+  std::vector<char> shared;         // per tile: in a shared launch?
+  std::vector<std::vector<int>> groups;  // tiles of each shared launch
+};
+
+int plan_batch(const na3d_tile* tiles, int n, int NH, int HD, int KT, int KH, int KW,
+               BatchPlan* bp) {
+  bp->plan.assign(n, Launch{});
+  bp->shared.assign(n, 0);
+  bp->groups.clear();
+  bp->variant = -1;
+  if (n == 0) return NA3D_OK;
+  std::vector<Geom> geo(n);
+  int lead = 0;
+  for (int i = 0; i < n; ++i) {
+    const na3d_tile& t = tiles[i];
+    const int rc = check_sizes(t.B, t.T, t.H, t.W, NH, HD, KT, KH, KW);
+    if (rc != NA3D_OK) return rc;
+    geo[i] = tile_geom(t, NH, HD, KT, KH, KW);
+    Strides st[4];
+    contiguous_all(geo[i], st);
+    geo[i].kv_span = kv_span_bytes(st[1], t.H, t.W, HD);
+    const int64_t wi = (int64_t)t.B * t.T * t.H * t.W, wl = (int64_t)tiles[lead].B *
+                                                          tiles[lead].T * tiles[lead].H * tiles[lead].W;
+    if (wi > wl) lead = i;
+  }
+  Launch ll;
+  if (make_plan(geo[lead], &ll) != NA3D_OK) return NA3D_ERR_SHAPE;
+  if (ll.family == 2) bp->variant = ll.variant;
+  // a tile in a shared launch needs only its share of the launch's
+  // workgroups: its runs stay as long as the whole batch allows
+  double total = 0;
+  for (int i = 0; i < n; ++i) total += (double)tiles[i].B * tiles[i].T * tiles[i].H * tiles[i].W;
+  std::vector<int> cur;
+  int64_t cur_wgs = 0;
+  for (int i = 0; i < n; ++i) {
+    Launch l;
+    const double share = (double)tiles[i].B * tiles[i].T * tiles[i].H * tiles[i].W / total;
+    const int target = std::max(1, (int)(kTargetWorkgroups * share));
+    if (bp->variant >= 0 && plan_roll(bp->variant, geo[i], 0, &l, target)) {
+      bp->plan[i] = l;
+      bp->shared[i] = 1;
+      if (!cur.empty() && ((int)cur.size() == kMaxBatch || cur_wgs + l.wgs > 0x7fffffff)) {
+        bp->groups.push_back(cur);
+        cur.clear();
+        cur_wgs = 0;
+      }
+      cur.push_back(i);
+      cur_wgs += l.wgs;
+    } else {
+      if (make_plan(geo[i], &l) != NA3D_OK) return NA3D_ERR_SHAPE;
+      bp->plan[i] = l;
+    }
+  }
+  if (!cur.empty()) bp->groups.push_back(cur);
+  return NA3D_OK;
+}
+
+int batch_impl(const na3d_tile* tiles, int n, int NH, int HD, int KT, int KH, int KW,
+               void* stream) {
+  int rc = check_batch(tiles, n, NH, HD, KT, KH, KW);
+  if (rc != NA3D_OK || n == 0) return rc;
+  BatchPlan bp;
+  rc = plan_batch(tiles, n, NH, HD, KT, KH, KW, &bp);
+  if (rc != NA3D_OK) return rc;
+  rc = device_ok();
+  if (rc != NA3D_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (const std::vector<int>& grp : bp.groups) {
+    RollBatch bt;
+    bt.n = (int)grp.size();
+    Launch l = bp.plan[grp[0]];
+    int64_t off = 0;
+    for (int j = 0; j < bt.n; ++j) {
+      const na3d_tile& t = tiles[grp[j]];
+      const Launch& lt = bp.plan[grp[j]];
+      BatchTile& e = bt.t[j];
+      e.q = static_cast<const uint16_t*>(t.q);
+      e.k = static_cast<const uint16_t*>(t.k);
+      e.v = static_cast<const uint16_t*>(t.v);
+      e.o = static_cast<uint16_t*>(t.out);
+      e.B = t.B; e.T = t.T; e.H = t.H; e.W = t.W;
+      e.wg_off = (int)off;
+      e.tiles_t = lt.tiles_t; e.tiles_h = lt.tiles_h; e.tiles_w = lt.tiles_w;
+      e.tc = lt.tile_t; e.ta = lt.ta; e.tz = lt.tz; e.nruns = lt.nruns; e.rpw = lt.rpw;
+      e.lds_rows = lt.lds_rows;
+      off += lt.wgs;
+      l.lds_rows = std::max(l.lds_rows, lt.lds_rows);
+      l.lds_bytes = std::max(l.lds_bytes, lt.lds_bytes);
+    }
+    l.wgs = off;
+    Problem p;
+    p.NH = NH; p.KT = KT; p.KH = KH; p.KW = KW;
+    if (launch_roll_batch(p, l, bt, HD, s) != 0) return NA3D_ERR_LAUNCH;
+  }
+  for (int i = 0; i < n; ++i) {
+    if (bp.shared[i]) continue;
+    const na3d_tile& t = tiles[i];
+    const Geom g = tile_geom(t, NH, HD, KT, KH, KW);
+    Strides st[4];
+    contiguous_all(g, st);
+    rc = run(t.q, t.k, t.v, t.out, g, st, bp.plan[i], stream);
+    if (rc != NA3D_OK) return rc;
+  }
+  return NA3D_OK;
+}
+
 int rms_impl(const void* x, const void* w, void* y, int rows, int dim, float eps, int wgs,
              void* stream) {
   int rc = rms_check(x, w, y, rows, dim, eps);
@@ -615,6 +768,36 @@ int na3d_rms_norm(const void* x, const void* weight, void* y, int rows, int dim,
 int na3d_rms_norm_config(const void* x, const void* weight, void* y, int rows, int dim,
                          float eps, int workgroups, void* stream) {
   return rms_impl(x, weight, y, rows, dim, eps, workgroups, stream);
+}
+
+int na3d_check_args_batch(const na3d_tile* tiles, int n, int NH, int HD, int KT, int KH,
+                          int KW) {
+  return check_batch(tiles, n, NH, HD, KT, KH, KW);
+}
+
+int na3d_plan_batch(const na3d_tile* tiles, int n, int NH, int HD, int KT, int KH, int KW,
+                    int* plan) {
+  if (!plan) return NA3D_ERR_NULL;
+  if (n < 0) return NA3D_ERR_SHAPE;
+  if (n > 0 && !tiles) return NA3D_ERR_NULL;
+  BatchPlan bp;
+  const int rc = plan_batch(tiles, n, NH, HD, KT, KH, KW, &bp);
+  if (rc != NA3D_OK) return rc;
+  int solo = 0, shared = 0;
+  for (int i = 0; i < n; ++i) (bp.shared[i] ? shared : solo) += 1;
+  plan[0] = (int)bp.groups.size() + solo;
+  plan[1] = bp.groups.empty() ? -1 : bp.variant;
+  plan[2] = shared;
+  int64_t w = 0;
+  if (!bp.groups.empty())
+    for (int i : bp.groups[0]) w += bp.plan[i].wgs;
+  plan[3] = (int)w;
+  return NA3D_OK;
+}
+
+int na3d_fwd_batch(const na3d_tile* tiles, int n, int NH, int HD, int KT, int KH, int KW,
+                   void* stream) {
+  return batch_impl(tiles, n, NH, HD, KT, KH, KW, stream);
 }
 
 }  // extern "C"
