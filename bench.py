@@ -66,6 +66,8 @@ def parse():
                     help="headline run without the batched decoder-tiles companion measurement")
     ap.add_argument("--no-rms-norm", action="store_true",
                     help="headline run without the RMSNorm block-norm companion measurement")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache single-launch timings (counter runs)")
     ap.add_argument("--no-check", action="store_true",
                     help="skip the sampled parity check before timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -115,6 +117,33 @@ def time_kernel(fn, steps, warmup):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     return wall_ms, e0.elapsed_time(e1) / steps
+
+
+def per_launch_us(fn, reps, cold_bytes=0):
+    """Median and minimum of single-launch kernel times (HIP events around
+    each launch on the launch stream).  cold_bytes > 0: before every launch a
+    buffer of that size is overwritten and the GPU drained, so the launch
+    starts with the inputs evicted from L2 and the 256 MB MALL."""
+    import statistics
+
+    import torch
+
+    stream = torch.cuda.current_stream()
+    scratch = None
+    if cold_bytes:
+        scratch = torch.empty(cold_bytes // 4, dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for i, (e0, e1) in enumerate(evs):
+        if scratch is not None:
+            scratch.fill_(float(i))
+            torch.cuda.synchronize()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
+    return {"median": round(statistics.median(t), 2), "min": round(min(t), 2), "reps": reps}
 
 
 def sampled_check(q, k, v, window, out, seed, npts=400):
@@ -171,7 +200,7 @@ def cpu_baseline(host_inputs, window, seed, target_s):
     }
 
 
-def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0):
+def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0, cold=True):
     import torch
 
     import neighborhood_attention_amd as na
@@ -191,6 +220,10 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0):
             raise SystemExit("parity gate failed on %s: rel_l2=%.3e max_abs=%.3e"
                              % (name, rel, mab))
     wall_ms, kern_ms = time_kernel(fn, steps, warmup)
+    single = {"warm": per_launch_us(fn, steps)}
+    if cold:
+        single["cold"] = per_launch_us(fn, max(steps // 2, 5), cold_bytes=512 << 20)
+        single["cold"]["between_launches"] = "512 MiB written, GPU drained"
     tflops = w.flops / (wall_ms * 1e-3) / 1e12
     kern_s = kern_ms * 1e-3
     ai = w.flops / w.bytes
@@ -237,6 +270,7 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0):
             "traffic_bytes_per_launch": tbytes,
         },
         "kernel_us": round(kern_ms * 1e3, 2),
+        "per_launch_us": single,
         "parity_sampled": {"rel_l2": rel, "max_abs": mab},
     }
     if cpu and host is not None:
@@ -432,6 +466,18 @@ def bench_batch(steps, warmup):
     }
 
 
+def copy_bandwidth(nbytes=1 << 30, reps=20):
+    """A plain device-to-device copy (torch's), GB/s counting the bytes read
+    and written: the streaming rate a simple kernel reaches on this GPU,
+    beside the 8 TB/s specification."""
+    import torch
+
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    _, ms = time_kernel(lambda: dst.copy_(src), reps, 3)
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
 def copy_calibration(nbytes):
     """A plain device copy of a known size, for scaling memory counters."""
     import torch
@@ -467,18 +513,20 @@ def main():
             print(json.dumps(rec), flush=True)
         return 0
     rec = bench_workload(args.workload, args.steps, args.warmup, check=not args.no_check,
-                         cpu=not args.no_cpu_baseline, cpu_s=args.cpu_seconds)
+                         cpu=not args.no_cpu_baseline, cpu_s=args.cpu_seconds,
+                         cold=not args.no_cold)
     if args.workload == HEADLINE and not args.no_large_window:
         # the metric also names the 11x11x11 window: report it beside the headline
         lw = bench_workload("large_window", args.steps, args.warmup, check=not args.no_check,
-                            cpu=False)
+                            cpu=False, cold=not args.no_cold)
         rec["large_window_11x11x11"] = {
             "value": lw["value"], "unit": "TFLOP/s", "mfma_peak_frac": lw["mfma_peak_frac"],
             "ms_per_step": lw["ms_per_step"], "kernel_us": lw["kernel_us"],
+            "per_launch_us": lw["per_launch_us"],
             "roofline": lw["roofline"], "parity_sampled": lw["parity_sampled"]}
         # the pages' anisotropic wide-window benchmark grid, (3,5,27)
         ww = bench_workload("wide_w27", args.steps, args.warmup, check=not args.no_check,
-                            cpu=False)
+                            cpu=False, cold=not args.no_cold)
         rec["wide_window_3x5x27"] = {
             "shape_BTHWNH_HD": ww["config"]["shape_BTHWNH_HD"], "value": ww["value"],
             "unit": "TFLOP/s", "kernel_us": ww["kernel_us"], "roofline": ww["roofline"],
@@ -487,6 +535,8 @@ def main():
         rec["fused_qkv_inputs"] = bench_fused(args.workload, args.steps, args.warmup)
     if args.workload == HEADLINE and not args.no_split:
         rec["query_box_split_2x2"] = bench_split(args.workload, args.steps, args.warmup)
+    if args.workload == HEADLINE:
+        rec["measured_copy_GBps"] = copy_bandwidth()
     if args.workload == HEADLINE and not args.no_batch:
         rec["decoder_tiles_batched"] = bench_batch(args.steps, args.warmup)
     if args.workload == HEADLINE and not args.no_rms_norm:
