@@ -28,6 +28,8 @@
  * Asynchrony: na3d_fwd enqueues its kernel on `stream` (a hipStream_t; NULL
  *   means the default stream) and returns without synchronising.  A fault
  *   during execution is reported by the caller's next synchronising call.
+ *   No entry point allocates, copies between host and device or
+ *   synchronises, so every call may be captured in a HIP graph.
  *
  * Errors: every function returns 0 on success or a negative NA3D_ERR_* code.
  *   All argument checks run before any device call, so a rejected call has

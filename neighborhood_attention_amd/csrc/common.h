@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <cstdint>
 
 namespace na3d {
@@ -197,6 +199,27 @@ struct RollBatch {
   int n;
   BatchTile t[kMaxBatch];
 };
+
+// Raise kernel KERN's dynamic LDS limit above the 64 KiB default, once per
+// device and size (the largest size set so far is remembered; one cache per
+// kernel, since KERN is a template argument), so that launches, also under
+// graph capture, make no other runtime call.
+template <auto KERN>
+int set_lds(int lds_bytes) {
+  if (lds_bytes <= 64 * 1024) return 0;
+  static std::atomic<int> done[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  if (done[dev].load(std::memory_order_relaxed) >= lds_bytes) return 0;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(KERN),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess)
+    return -1;
+  int prev = done[dev].load(std::memory_order_relaxed);
+  while (prev < lds_bytes &&
+         !done[dev].compare_exchange_weak(prev, lds_bytes, std::memory_order_relaxed)) {
+  }
+  return 0;
+}
 
 int launch_general(const Problem& p, const Launch& l, int hd, hipStream_t s);
 int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s);

@@ -289,11 +289,8 @@ constexpr int kQH = 4, kQW = 4, kWH = 2, kWW = 2;  // 8 x 8 query tile, 4 waves
 
 template <int HD>
 int launch_hd(const GeneralArgs& a, const Launch& l, hipStream_t stream) {
-  auto kern = na3d_fwd_general_kernel<HD, kQH, kQW, kWH, kWW>;
-  if (l.lds_bytes > 64 * 1024 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, l.lds_bytes) != hipSuccess)
-    return -1;
+  constexpr auto kern = na3d_fwd_general_kernel<HD, kQH, kQW, kWH, kWW>;
+  if (set_lds<kern>(l.lds_bytes) != 0) return -1;
   hipLaunchKernelGGL(kern, dim3((unsigned)l.wgs), dim3(l.threads), l.lds_bytes, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -777,28 +777,18 @@ na3d_fwd_roll_batch_kernel(const RollArgs shared, const RollBatch bt) {
 }
 
 // ------------------------------------------------------------------ launch
-template <class K>
-int set_lds(K kern, int lds_bytes) {
-  return lds_bytes > 64 * 1024 &&
-                 hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     lds_bytes) != hipSuccess
-             ? -1
-             : 0;
-}
-
 template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
 int launch_cfg(const RollArgs& a, const Launch& l, hipStream_t stream) {
-  auto kern = na3d_fwd_roll_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>;
-  if (set_lds(kern, l.lds_bytes) != 0) return -1;
+  constexpr auto kern = na3d_fwd_roll_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>;
+  if (set_lds<kern>(l.lds_bytes) != 0) return -1;
   hipLaunchKernelGGL(kern, dim3((unsigned)l.wgs), dim3(l.threads), l.lds_bytes, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
 int launch_batch_cfg(const RollArgs& a, const RollBatch& bt, const Launch& l, hipStream_t stream) {
-  auto kern = na3d_fwd_roll_batch_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>;
-  if (set_lds(kern, l.lds_bytes) != 0) return -1;
+  constexpr auto kern = na3d_fwd_roll_batch_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>;
+  if (set_lds<kern>(l.lds_bytes) != 0) return -1;
   hipLaunchKernelGGL(kern, dim3((unsigned)l.wgs), dim3(l.threads), l.lds_bytes, stream, a, bt);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
