@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--all", action="store_true",
                     help="one JSON line per workload (development use)")
+    ap.add_argument("--pages-grid", action="store_true",
+                    help="time the six grids of the aiter PR's Performance table at NH = 4, 8 "
+                         "and 32 (one JSON line each; development use)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -478,6 +481,44 @@ def copy_bandwidth(nbytes=1 << 30, reps=20):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
+# The grids of the aiter PR page's Performance table (bf16, B=1, HD=64; the
+# head count per row is not stated), with the page's gfx950 (MI350X) kernel
+# times in microseconds, which include a v.contiguous() copy.
+PAGES_GRID = (
+    ((18, 32, 48), (3, 7, 7), 1249),
+    ((36, 64, 96), (3, 5, 5), 1910),
+    ((40, 96, 96), (3, 5, 5), 3319),
+    ((16, 80, 32), (11, 11, 11), 1153),
+    ((79, 192, 192), (11, 11, 11), 99143),
+    ((4, 8, 128), (3, 5, 27), 40),
+)
+
+
+def bench_pages_grid(steps, warmup):
+    """Our kernel on the page's benchmark grids at NH = 4, 8, 32.  Yields one
+    record per (grid, NH)."""
+    import torch
+
+    import neighborhood_attention_amd as na
+    from na3d_inputs import make_inputs
+
+    for (T, H, W), ks, page_us in PAGES_GRID:
+        for NH in (4, 8, 32):
+            shape = (1, T, H, W, NH, 64)
+            q, k, v = make_inputs(shape, 60 + T + NH, "cuda")
+            out = torch.empty_like(q)
+            fn = lambda: na.fwd(q, k, v, ks, out=out)
+            n = max(3, min(steps, int(2e5 / max(page_us, 1))))
+            _, ms = time_kernel(fn, n, min(warmup, n))
+            flops = 4 * NH * T * H * W * ks[0] * ks[1] * ks[2] * 64
+            plan = na.plan(shape, ks)
+            yield {"grid_THW": [T, H, W], "window": list(ks), "NH": NH, "HD": 64,
+                   "kernel_us": round(ms * 1e3, 2), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+                   "page_gfx950_us": page_us, "variant": plan["variant"], "launches": n}
+            del q, k, v, out
+            torch.cuda.empty_cache()
+
+
 def copy_calibration(nbytes):
     """A plain device copy of a known size, for scaling memory counters."""
     import torch
@@ -504,6 +545,10 @@ def main():
         return 1
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return 0
+    if args.pages_grid:
+        for rec in bench_pages_grid(args.steps, args.warmup):
+            print(json.dumps(rec), flush=True)
         return 0
     if args.all:
         from na3d_inputs import WORKLOADS

@@ -285,8 +285,19 @@ int pick_roll(const Geom& g, Launch* l) {
     case 128: pref = p128; np = (int)(sizeof(p128) / sizeof(int)); break;
     default: pref = p256; np = 1; break;
   }
-  for (int i = 0; i < np; ++i)
-    if (plan_roll(pref[i], g, 0, l)) return 1;
+  for (int i = 0; i < np; ++i) {
+    if (!plan_roll(pref[i], g, 0, l)) continue;
+    // windows much wider than tall, on a grid large enough that the 8-wave
+    // two-buffer variant has four or more workgroups per CU: the 4-wave
+    // one-buffer variant of the same blocks is faster (measured on the
+    // (3,5,27) benchmark grid: 51 us against 60 us at 32 heads; equal at 16,
+    // slower at 8)
+    if (pref[i] == 51 && l->wgs >= 1024) {
+      Launch alt;
+      if (plan_roll(49, g, 0, &alt)) *l = alt;
+    }
+    return 1;
+  }
   return 0;
 }
 
