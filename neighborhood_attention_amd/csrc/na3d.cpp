@@ -296,6 +296,14 @@ int pick_roll(const Geom& g, Launch* l) {
       Launch alt;
       if (plan_roll(49, g, 0, &alt)) *l = alt;
     }
+    // mid-size windows on a grid with fewer than 1024 spatial tiles of the
+    // 8-wave variant: 4-wave workgroups fill the chip better (measured on
+    // the 18x32x48 (3,7,7) benchmark grid: 36-51 us against 38-57 us at 4
+    // and 8 heads; at 32 heads and on the decoder tile the 8-wave one wins)
+    if (pref[i] == 42 && l->wgs / std::max(l->tiles_t, 1) < 1024) {
+      Launch alt;
+      if (plan_roll(34, g, 0, &alt)) *l = alt;
+    }
     return 1;
   }
   return 0;
