@@ -280,10 +280,10 @@ int na3d_check_args_rms_norm(const void* x, const void* weight, const void* y,
                              int rows, int dim, float eps);
 
 /*
- * na3d_rms_norm with an explicit grid of `workgroups` workgroups of four
- * waves (each wave normalises rows wave, wave + 4*workgroups, ...), for
- * tuning sweeps and for testing the multi-row path; 0 = automatic,
- * negative or above 2^24 = NA3D_ERR_CONFIG.
+ * na3d_rms_norm with an explicit grid of `workgroups` workgroups of w waves,
+ * w = 8 for dim <= 4096 and 4 above (each wave normalises rows wave,
+ * wave + w*workgroups, ...), for tuning sweeps and for testing the multi-row
+ * path; 0 = automatic, negative or above 2^24 = NA3D_ERR_CONFIG.
  */
 int na3d_rms_norm_config(const void* x, const void* weight, void* y, int rows,
                          int dim, float eps, int workgroups, void* stream);

@@ -28,7 +28,11 @@
 namespace na3d {
 namespace {
 
-constexpr int kRmsWaves = 4;  // waves per workgroup
+// Waves per workgroup: 8, except for the longest rows, whose 400+ registers
+// per lane leave room for one wave per SIMD only (a workgroup must fit one
+// CU's four SIMDs).
+template <int KCH>
+constexpr int rms_waves() { return KCH >= 16 ? 4 : 8; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 8 bf16
 
@@ -106,7 +110,8 @@ __device__ __forceinline__ void norm_row(u32x4 (&v)[KCH], const u32x4 (&w)[KCH],
 // prefetch row is clamped to the last row, so the loads are unconditional
 // (a wave's final prefetch re-reads that one row, which the caches hold).
 template <int KCH, bool FULL>
-__global__ void __launch_bounds__(64 * kRmsWaves) rms_norm_kernel(const RmsArgs a) {
+__global__ void __launch_bounds__(64 * rms_waves<KCH>()) rms_norm_kernel(const RmsArgs a) {
+  constexpr int kRmsWaves = rms_waves<KCH>();
   const int lane = threadIdx.x & 63;
   const int first = __builtin_amdgcn_readfirstlane(blockIdx.x * kRmsWaves + (threadIdx.x >> 6));
   const int step = gridDim.x * kRmsWaves;
@@ -147,14 +152,17 @@ __global__ void __launch_bounds__(64 * kRmsWaves) rms_norm_kernel(const RmsArgs 
   }
 }
 
-// wgs == 0: about two rows per wave, many more waves than the GPU holds at
-// once; the hardware hands the late workgroups to whichever CUs free up
-// first, which evens out the end of the launch better than a grid sized to
-// what is resident (measured: 2-4% faster on 24576 x 4096).
+// wgs == 0: about one and a half rows per wave, many more waves than the
+// GPU holds at once; the hardware hands the late workgroups to whichever CUs
+// free up first, which evens out the end of the launch better than a grid
+// sized to what is resident (measured on 24576 x 4096: 56.9 us with 8-wave
+// workgroups at 1.5 rows per wave, 58.0 us with 4-wave ones at 2 rows, 58.6
+// us with a resident-sized grid).
 template <int KCH, bool FULL>
 int launch_kch(const RmsArgs& a, int wgs, hipStream_t s) {
+  constexpr int kRmsWaves = rms_waves<KCH>();
   if (wgs == 0) {
-    const int64_t g = ((int64_t)a.rows + 2 * kRmsWaves - 1) / (2 * kRmsWaves);
+    const int64_t g = (2 * (int64_t)a.rows + 3 * kRmsWaves - 1) / (3 * kRmsWaves);
     wgs = (int)(g < (1 << 20) ? g : (1 << 20));  // beyond that, waves stride over rows
   }
   hipLaunchKernelGGL((rms_norm_kernel<KCH, FULL>), dim3(wgs), dim3(64 * kRmsWaves), 0, s, a);
