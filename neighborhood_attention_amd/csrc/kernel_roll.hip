@@ -13,7 +13,7 @@
 // the staged halo rows, and every K/V operand address is a lane constant plus
 // a compile-time tile offset.
 //
-// The WG streams the key planes of its run in order.  Each plane's K/V halo
+// The WG streams the key planes of its runs in order.  Each plane's K/V halo
 // is staged in LDS once, with direct global->LDS loads (global_load_lds
 // dwordx4), into one or two plane buffers (with two, plane t'+1 is in flight
 // while plane t' is computed).  Staged rows are unpadded and XOR-swizzled in
@@ -36,14 +36,20 @@
 //   S^T = K . Q^T + mask    bf16 MFMA 16x16x32, seeded with the window mask
 //                           (0 or -2^100): one MFMA per tile of the mask,
 //                           kept as bf16 in registers, against the identity
-//   softmax                 one exact max over the group's scores, one
-//                           rescale of the running output, then exp2
-//   O^T += V^T . P^T        bf16 MFMA 16x16x32 per pair of tiles (16x16x16
-//                           for an odd last tile); the S^T accumulator layout
-//                           is already the P^T operand, V^T comes from the
-//                           transpose read
+//   softmax                 one exact max over the group's scores, a
+//                           rescale of the running output only when the max
+//                           rises by more than kRescale, then exp2
+//   O^T += V^T . P^T        bf16 MFMA 16x16x32 per pair of tiles (an odd
+//                           last tile is paired with zero weights); the S^T
+//                           accumulator layout is already the P^T operand,
+//                           V^T comes from the transpose read
 // Rows past the staged halo are zeroed once, so every row read holds finite
 // values and masked keys contribute exactly zero.
+//
+// The kernel body (roll_body) serves two entry kernels: one grid per launch,
+// and many independent grids per launch (tiles of a decoder's tile grid),
+// where each workgroup first looks up its tile in a table passed with the
+// kernel arguments.
 //
 // Global memory traffic is arranged so that compute never waits on it:
 // a query plane's Q is fetched one key plane ahead into spare registers, and
