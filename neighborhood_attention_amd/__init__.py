@@ -119,6 +119,17 @@ def load(path: str = LIB_PATH):
         return lib
 
 
+def _on_device(dev, call):
+    """Run call(stream) with dev current and its current stream; the device
+    switch is skipped when dev already is the current device."""
+    import torch
+
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        return call(torch.cuda.current_stream(dev).cuda_stream)
+    with torch.cuda.device(dev):
+        return call(torch.cuda.current_stream(dev).cuda_stream)
+
+
 def status_string(status: int) -> str:
     return load().na3d_status_string(int(status)).decode()
 
@@ -246,10 +257,9 @@ def fwd(q, k, v, kernel_size, out=None, config=None):
     strides = None
     if not all(t.is_contiguous() for t in tensors):
         strides = [tuple(int(x) for x in t.stride()[:5]) for t in tensors]
-    with torch.cuda.device(q.device):
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-        fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), q.shape,
-                kernel_size, stream, config, strides)
+    _on_device(q.device, lambda stream: fwd_raw(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), q.shape, kernel_size, stream,
+        config, strides))
     return out
 
 
@@ -288,10 +298,9 @@ def fwd_subgrid(q, k, v, kernel_size, offset, out=None, config=None):
     strides = None
     if not all(t.is_contiguous() for t in tensors):
         strides = [tuple(int(x) for x in t.stride()[:5]) for t in tensors]
-    with torch.cuda.device(q.device):
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-        fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), k.shape,
-                kernel_size, stream, config, strides, box)
+    _on_device(q.device, lambda stream: fwd_raw(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), k.shape, kernel_size, stream,
+        config, strides, box))
     return out
 
 
@@ -342,10 +351,9 @@ def rms_norm(x, weight=None, eps: float = 1e-6, out=None, workgroups=None):
     elif (out.shape != x.shape or out.dtype != torch.bfloat16 or out.device != x.device
           or not out.is_contiguous()):
         raise ValueError("out must be a contiguous bf16 tensor shaped like x")
-    with torch.cuda.device(x.device):
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-        rms_norm_raw(x.data_ptr(), None if weight is None else weight.data_ptr(),
-                     out.data_ptr(), rows, dim, eps, stream, workgroups)
+    _on_device(x.device, lambda stream: rms_norm_raw(
+        x.data_ptr(), None if weight is None else weight.data_ptr(), out.data_ptr(), rows, dim,
+        eps, stream, workgroups))
     return out
 
 
@@ -421,7 +429,5 @@ def fwd_batch(qkv, kernel_size, outs=None):
         raise ValueError("outs must be contiguous bf16 tensors shaped like each q")
     tiles = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), q.shape[:4])
              for (q, k, v), o in zip(qkv, outs)]
-    with torch.cuda.device(dev):
-        stream = torch.cuda.current_stream(dev).cuda_stream
-        fwd_batch_raw(tiles, NH, HD, kernel_size, stream)
+    _on_device(dev, lambda stream: fwd_batch_raw(tiles, NH, HD, kernel_size, stream))
     return outs

@@ -7,6 +7,8 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/na3d.h"
@@ -418,6 +420,45 @@ int run(const void* q, const void* k, const void* v, void* out, const Geom& g, c
   return rc == 0 ? NA3D_OK : NA3D_ERR_LAUNCH;
 }
 
+// Plans by geometry and requested configuration: the planner's run search
+// costs a few microseconds per call, comparable to a small grid's kernel, so
+// repeated calls with the same sizes reuse the first plan.
+struct PlanKey {
+  int v[19];
+  int64_t span;
+  bool operator==(const PlanKey& o) const {
+    return span == o.span && std::memcmp(v, o.v, sizeof(v)) == 0;
+  }
+};
+struct PlanKeyHash {
+  size_t operator()(const PlanKey& k) const {
+    uint64_t h = 1469598103934665603ull ^ (uint64_t)k.span;
+    for (int x : k.v) h = (h ^ (uint32_t)x) * 1099511628211ull;
+    return (size_t)h;
+  }
+};
+std::mutex g_plan_mu;
+std::unordered_map<PlanKey, std::pair<int, Launch>, PlanKeyHash> g_plans;
+
+int cached_plan(const Geom& g, int family, int variant, int tile_t, Launch* l) {
+  const PlanKey key{{g.B, g.T, g.H, g.W, g.NH, g.HD, g.KT, g.KH, g.KW, g.box.t0, g.box.h0,
+                     g.box.w0, g.box.Tq, g.box.Hq, g.box.Wq, family, variant, tile_t, 0},
+                    g.kv_span};
+  {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    const auto it = g_plans.find(key);
+    if (it != g_plans.end()) {
+      *l = it->second.second;
+      return it->second.first;
+    }
+  }
+  const int rc = make_plan_config(g, family, variant, tile_t, l);
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  if (g_plans.size() >= 4096) g_plans.clear();
+  g_plans.emplace(key, std::make_pair(rc, *l));
+  return rc;
+}
+
 // Checks, plans and launches one call.
 int fwd_impl(const void* q, const void* k, const void* v, void* out, Geom g, const Strides* st,
              int family, int variant, int tile_t, void* stream) {
@@ -425,7 +466,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, Geom g, con
   if (rc != NA3D_OK) return rc;
   g.kv_span = kv_span_bytes(st[1], g.H, g.W, g.HD);
   Launch l;
-  rc = make_plan_config(g, family, variant, tile_t, &l);
+  rc = cached_plan(g, family, variant, tile_t, &l);
   if (rc != NA3D_OK) return rc;
   return run(q, k, v, out, g, st, l, stream);
 }
