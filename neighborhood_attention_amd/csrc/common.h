@@ -165,7 +165,9 @@ struct Launch {
   X(48, 128, 2, 8, 2, 4, 1, 7, 1, 1, 0) \
   X(49, 64, 2, 8, 1, 4, 1, 13, 1, 1, 0) \
   X(50, 64, 2, 8, 2, 4, 1, 13, 1, 1, 0) \
-  X(51, 64, 2, 8, 2, 4, 1, 13, 1, 2, 0)
+  X(51, 64, 2, 8, 2, 4, 1, 13, 1, 2, 0) \
+  X(52, 256, 2, 8, 1, 4, 1, 7, 1, 1, 0) \
+  X(53, 256, 4, 4, 1, 4, 1, 7, 1, 1, 0)
 
 struct RollVariant {
   int hd, qh, qw, wh, wt, ns, nk, ng, nbuf, occ;
