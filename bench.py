@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-large-window", action="store_true",
                     help="headline run without the 11x11x11 companion measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="headline run without the full-scale, narrow and tiny companions")
     ap.add_argument("--no-fused", action="store_true",
                     help="headline run without the fused-QKV input companion measurement")
     ap.add_argument("--no-split", action="store_true",
@@ -237,6 +239,10 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0, cold=T
         achieved, peak, unit = w.flops / kern_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     plan = na.plan(w.shape, w.window)
     tbytes = measured_traffic(name)  # HBM bytes per launch from the counters, if current
+    hashes = None
+    if host is not None:
+        from na3d_inputs import sha256_of
+        hashes = {n_: sha256_of(t) for n_, t in zip("qkv", host)}
     rec = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -275,10 +281,24 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0, cold=T
         "kernel_us": round(kern_ms * 1e3, 2),
         "per_launch_us": single,
         "parity_sampled": {"rel_l2": rel, "max_abs": mab},
+        "inputs_sha256": hashes,
     }
     if cpu and host is not None:
-        rec["cpu_baseline"] = cpu_baseline(host, w.window, w.seed, cpu_s)
+        cb = cpu_baseline(host, w.window, w.seed, cpu_s)
+        cb["cpu_model"] = cpu_model()
+        cb["gpu_over_oracle"] = round(tflops / cb["value"], 1) if cb["value"] > 0 else None
+        rec["cpu_baseline"] = cb
     return rec
+
+
+def companion(name, steps, warmup, cold=False):
+    """A further workload in the same run, reported beside the headline with
+    its own roofline (parity gate first, as for the headline)."""
+    rec = bench_workload(name, steps, warmup, check=True, cpu=False, cold=cold)
+    return {k: rec[k] for k in ("value", "unit", "mfma_peak_frac", "ms_per_step", "kernel_us",
+                                "per_launch_us", "roofline", "parity_sampled", "inputs_sha256")} | {
+        "shape_BTHWNH_HD": rec["config"]["shape_BTHWNH_HD"], "window": rec["config"]["window"],
+        "variant": rec["config"]["variant"], "workgroups": rec["config"]["workgroups"]}
 
 
 def bench_fused(name, steps, warmup):
@@ -481,6 +501,71 @@ def copy_bandwidth(nbytes=1 << 30, reps=20):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
+def gemm_tflops(n=8192, reps=20):
+    """A plain bf16 GEMM (torch.matmul, i.e. hipBLASLt) of n x n x n: the MFMA
+    rate a tuned library kernel reaches on this GPU, beside the 2.5 PFLOP/s
+    specification."""
+    import torch
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    a = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    _, ms = time_kernel(lambda: torch.matmul(a, b, out=c), reps, 3)
+    return round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def gpu_clocks():
+    """Current shader / memory clocks as the SMI tools report them (MHz), or
+    the reason they are not available."""
+    import subprocess
+
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.TimeoutExpired) as e:
+            last = "%s: %s" % (cmd[0], type(e).__name__)
+            continue
+        if r.returncode != 0:
+            last = "%s: exit %d" % (cmd[0], r.returncode)
+            continue
+        txt = r.stdout
+        found = {}
+        for key, pat in (("sclk_MHz", r'"(?:gfx_0|gfx|sclk)[^"]*"[^{}]*?"clk"\s*:\s*\{?[^}]*?"value"\s*:\s*(\d+)'),
+                         ("mclk_MHz", r'"(?:mem_0|mem|mclk)[^"]*"[^{}]*?"clk"\s*:\s*\{?[^}]*?"value"\s*:\s*(\d+)'),
+                         ("sclk_MHz", r'sclk[^"]*"\s*:\s*"\(?(\d+)\s*Mhz'),
+                         ("mclk_MHz", r'mclk[^"]*"\s*:\s*"\(?(\d+)\s*Mhz')):
+            m = re.search(pat, txt, re.I | re.S)
+            if m and key not in found:
+                found[key] = int(m.group(1))
+        found["source"] = " ".join(cmd)
+        return found
+    return {"source": "unavailable (%s)" % last}
+
+
+def provenance():
+    import torch
+
+    return {
+        "torch": torch.__version__, "hip": torch.version.hip,
+        "gpu": torch.cuda.get_device_name(0),
+        "cpu_model": cpu_model(), "host_threads": len(os.sched_getaffinity(0)),
+        "clocks": gpu_clocks(),
+    }
+
+
 # The grids of the aiter PR page's Performance table (bf16, B=1, HD=64; the
 # head count per row is not stated), with the page's gfx950 (MI350X) kernel
 # times in microseconds, which include a v.contiguous() copy.
@@ -568,7 +653,9 @@ def main():
             "value": lw["value"], "unit": "TFLOP/s", "mfma_peak_frac": lw["mfma_peak_frac"],
             "ms_per_step": lw["ms_per_step"], "kernel_us": lw["kernel_us"],
             "per_launch_us": lw["per_launch_us"],
-            "roofline": lw["roofline"], "parity_sampled": lw["parity_sampled"]}
+            "roofline": lw["roofline"], "parity_sampled": lw["parity_sampled"],
+            "inputs_sha256": lw["inputs_sha256"], "variant": lw["config"]["variant"],
+            "workgroups": lw["config"]["workgroups"]}
         # the pages' anisotropic wide-window benchmark grid, (3,5,27)
         ww = bench_workload("wide_w27", args.steps, args.warmup, check=not args.no_check,
                             cpu=False, cold=not args.no_cold)
@@ -576,12 +663,31 @@ def main():
             "shape_BTHWNH_HD": ww["config"]["shape_BTHWNH_HD"], "value": ww["value"],
             "unit": "TFLOP/s", "kernel_us": ww["kernel_us"], "roofline": ww["roofline"],
             "parity_sampled": ww["parity_sampled"], "variant": ww["config"]["variant"]}
+    if args.workload == HEADLINE and not args.no_configs:
+        # the remaining workloads of the metric's configuration list, each with
+        # its own roofline: full scale (HD 128, x8 key outliers; fewer
+        # launches: ~5 ms each), the two narrow edge tiles and the tiny grid
+        rec["full_scale"] = companion("full_scale", max(5, min(args.steps, 20)),
+                                      min(args.warmup, 3))
+        for nm in ("narrow_w7", "narrow_w5", "tiny"):
+            rec[nm] = companion(nm, args.steps, args.warmup)
     if args.workload == HEADLINE and not args.no_fused:
         rec["fused_qkv_inputs"] = bench_fused(args.workload, args.steps, args.warmup)
     if args.workload == HEADLINE and not args.no_split:
         rec["query_box_split_2x2"] = bench_split(args.workload, args.steps, args.warmup)
     if args.workload == HEADLINE:
         rec["measured_copy_GBps"] = copy_bandwidth()
+        rec["measured_gemm_TFLOPs"] = gemm_tflops()
+        # roofline fractions against what a device copy and a library GEMM
+        # reach here, beside the specification peaks
+        meas = {"hbm": rec["measured_copy_GBps"], "mfma": rec["measured_gemm_TFLOPs"]}
+        for sub in [rec] + [rec[k] for k in ("large_window_11x11x11", "wide_window_3x5x27",
+                                             "full_scale", "narrow_w7", "narrow_w5", "tiny")
+                            if k in rec]:
+            rf = sub["roofline"]
+            rf["measured_peak"] = meas[rf["bound"]]
+            rf["frac_of_measured_peak"] = round(rf["achieved"] / meas[rf["bound"]], 4)
+        rec["provenance"] = provenance()
     if args.workload == HEADLINE and not args.no_batch:
         rec["decoder_tiles_batched"] = bench_batch(args.steps, args.warmup)
     if args.workload == HEADLINE and not args.no_rms_norm:

@@ -35,6 +35,20 @@
  *   All argument checks run before any device call, so a rejected call has
  *   no effect on the device.  Nothing is printed and no exception crosses
  *   the ABI.
+ *
+ * Library state: the library keeps three process-wide caches, each a
+ *   memo of a pure function of its key, so no result depends on what they
+ *   hold and calls from several threads are safe (a mutex guards the first,
+ *   atomics the others):
+ *   - launch plans keyed by every size, box, requested configuration and
+ *     K/V span of a call (at most 4096 entries; when full it is emptied and
+ *     refilled); the planner is deterministic, so a cached plan is the plan
+ *     the call would compute;
+ *   - per device, whether it is gfx950;
+ *   - per kernel instantiation and device, the largest dynamic-LDS limit
+ *     already raised with hipFuncSetAttribute (so a later launch, also under
+ *     graph capture, makes no other runtime call).
+ *   None of them holds a caller's pointer or device memory.
  */
 #ifndef NA3D_H_
 #define NA3D_H_

@@ -148,4 +148,4 @@ def workload_inputs(name: str, device="cpu"):
 def sha256_of(t: torch.Tensor) -> str:
     """SHA-256 of a tensor's bytes (recorded next to results)."""
     a = t.detach().to("cpu").contiguous().view(torch.uint8).numpy()
-    return hashlib.sha256(a.tobytes()).hexdigest()
+    return hashlib.sha256(memoryview(a)).hexdigest()

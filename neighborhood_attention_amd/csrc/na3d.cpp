@@ -37,12 +37,22 @@ bool overlaps2(const void* a, size_t na, const void* b, size_t nb) {
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// *r = a * b + c without signed overflow; false when it would overflow.
+bool mul_add(int64_t a, int64_t b, int64_t c, int64_t* r) {
+  int64_t p;
+  if (__builtin_mul_overflow(a, b, &p)) return false;
+  return !__builtin_add_overflow(p, c, r);
+}
+
 int check_sizes(int B, int T, int H, int W, int NH, int HD, int KT, int KH, int KW) {
   if (B < 1 || T < 1 || H < 1 || W < 1 || NH < 1 || HD < 1) return NA3D_ERR_SHAPE;
   if (!head_dim_ok(HD)) return NA3D_ERR_HEAD_DIM;
-  // per-plane and per-batch element counts stay addressable in 32/64 bit
+  // per-plane and per-batch element counts stay addressable in 32/64 bit;
+  // every product is overflow-checked (the factors are arbitrary ints)
   if ((int64_t)T * H * W > ((int64_t)1 << 30)) return NA3D_ERR_SHAPE;
-  if ((int64_t)B * T * H * W * NH * HD > ((int64_t)1 << 61)) return NA3D_ERR_SHAPE;
+  int64_t n = (int64_t)T * H * W;
+  for (const int f : {B, NH, HD})
+    if (!mul_add(n, f, 0, &n) || n > ((int64_t)1 << 61)) return NA3D_ERR_SHAPE;
   if (KT < 1 || KH < 1 || KW < 1 || KT > T || KH > H || KW > W) return NA3D_ERR_WINDOW;
   return NA3D_OK;
 }
@@ -57,10 +67,15 @@ Strides contiguous(int T, int H, int W, int NH, int HD) {
   return s;
 }
 
-// Element offset of the last element of a tensor, plus one.
+// Element offset of the last element of a tensor, plus one, or -1 when it
+// does not fit in 62 bits (strides are >= 0 and sizes >= 1 here).
 int64_t extent(const Strides& s, int B, int T, int H, int W, int NH, int HD) {
-  return (int64_t)(B - 1) * s.b + (int64_t)(T - 1) * s.t + (int64_t)(H - 1) * s.h +
-         (int64_t)(W - 1) * s.w + (int64_t)(NH - 1) * s.n + HD;
+  int64_t e = HD;
+  const int64_t str[5] = {s.b, s.t, s.h, s.w, s.n};
+  const int ext[5] = {B, T, H, W, NH};
+  for (int i = 0; i < 5; ++i)
+    if (!mul_add(str[i], (int64_t)ext[i] - 1, e, &e)) return -1;
+  return e < ((int64_t)1 << 62) ? e : -1;
 }
 
 // Bytes spanned by the spatial (H, W) part of one K/V plane of one head: the
@@ -368,14 +383,18 @@ int check_strides(const void* q, const void* k, const void* v, const void* out, 
       const int a = idx[j];
       if (ext[a] == 1) continue;
       if (str[a] < span) return NA3D_ERR_STRIDE;
-      span = str[a] * (ext[a] - 1) + span;
+      if (!mul_add(str[a], ext[a] - 1, span, &span)) return NA3D_ERR_STRIDE;
     }
   }
-  const size_t bq = 2 * (size_t)extent(st[0], g.B, bx.Tq, bx.Hq, bx.Wq, g.NH, g.HD);
-  const size_t bo = 2 * (size_t)extent(st[3], g.B, bx.Tq, bx.Hq, bx.Wq, g.NH, g.HD);
-  if (overlaps2(out, bo, q, bq) ||
-      overlaps2(out, bo, k, 2 * (size_t)extent(st[1], g.B, g.T, g.H, g.W, g.NH, g.HD)) ||
-      overlaps2(out, bo, v, 2 * (size_t)extent(st[2], g.B, g.T, g.H, g.W, g.NH, g.HD)))
+  // element extents (-1: beyond what any buffer can span)
+  const int64_t eq = extent(st[0], g.B, bx.Tq, bx.Hq, bx.Wq, g.NH, g.HD);
+  const int64_t ek = extent(st[1], g.B, g.T, g.H, g.W, g.NH, g.HD);
+  const int64_t ev = extent(st[2], g.B, g.T, g.H, g.W, g.NH, g.HD);
+  const int64_t eo = extent(st[3], g.B, bx.Tq, bx.Hq, bx.Wq, g.NH, g.HD);
+  if (eq < 0 || ek < 0 || ev < 0 || eo < 0) return NA3D_ERR_STRIDE;
+  const size_t bo = 2 * (size_t)eo;
+  if (overlaps2(out, bo, q, 2 * (size_t)eq) || overlaps2(out, bo, k, 2 * (size_t)ek) ||
+      overlaps2(out, bo, v, 2 * (size_t)ev))
     return NA3D_ERR_OVERLAP;
   return NA3D_OK;
 }

@@ -101,6 +101,16 @@ def test_oversized_grid():
     assert check(shape=(1, 2048, 2048, 2048, 1, 16), ks=(1, 1, 1)) == na.NA3D_ERR_SHAPE
 
 
+def test_element_count_overflow_is_rejected():
+    """A 2^69-element tensor whose count wraps to 0 in 64-bit arithmetic
+    (B = 2^20, T = H = 2^10, W = 1, NH = 2^21, HD = 256) must not pass."""
+    big = (1 << 20, 1 << 10, 1 << 10, 1, 1 << 21, 256)
+    assert check(shape=big, ks=(1, 1, 1)) == na.NA3D_ERR_SHAPE
+    assert na.load().na3d_fwd(A, B_, C, O, *big, 1, 1, 1, None) == na.NA3D_ERR_SHAPE
+    assert check(shape=((1 << 31) - 1, 1, 1, 1, (1 << 31) - 1, 256), ks=(1, 1, 1)) \
+        == na.NA3D_ERR_SHAPE
+
+
 def test_status_strings():
     for code in range(0, -12, -1):
         s = na.status_string(code)

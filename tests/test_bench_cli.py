@@ -47,3 +47,10 @@ def test_pages_grid_table():
     for (T, H, W), ks, us in bench.PAGES_GRID:
         assert all(k <= n for k, n in zip(ks, (T, H, W))) and us > 0
     json.dumps([list(g) for g in bench.PAGES_GRID])
+
+
+def test_provenance_helpers_run_without_a_gpu():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+    clocks = bench.gpu_clocks()
+    assert "source" in clocks
+    json.dumps(clocks)

@@ -140,6 +140,34 @@ def test_oracle_vs_dense_masked_tiny_workload(oracle_mod):
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
 
 
+def test_weights_match_dense_masked_in_window_order(oracle_mod):
+    """Every weight row equals the row of the dense masked softmax P (numpy,
+    float64, mask from the interval search) read at the window's keys in
+    (dt, dh, dw) lexicographic order: pins both the values and their order."""
+    shape, ks = (1, 4, 5, 6, 2, 8), (3, 3, 5)
+    q, k, v = make_inputs(shape, seed=8)
+    wts, _ = oracle_mod.weights(q, k, v, ks)
+    qq, kk = f64(q), f64(k)
+    B, T, H, W, NH, HD = shape
+    mt, mh, mw = axis_mask(T, ks[0]), axis_mask(H, ks[1]), axis_mask(W, ks[2])
+    M = (mt[:, None, None, :, None, None] & mh[None, :, None, None, :, None]
+         & mw[None, None, :, None, None, :]).reshape(T * H * W, T * H * W)
+    N = T * H * W
+    flat = lambda t, h, w: (t * H + h) * W + w
+    for n in range(NH):
+        S = qq[0, ..., n, :].reshape(N, HD) @ kk[0, ..., n, :].reshape(N, HD).T
+        S = np.where(M, S, -np.inf)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        for t, h, w in itertools.product(range(T), range(H), range(W)):
+            st, sh, sw = (searched_start(t, ks[0], T), searched_start(h, ks[1], H),
+                          searched_start(w, ks[2], W))
+            keys = [flat(st + a, sh + b, sw + c) for a in range(ks[0])
+                    for b in range(ks[1]) for c in range(ks[2])]
+            np.testing.assert_allclose(wts[0, t, h, w, n], P[flat(t, h, w), keys],
+                                       rtol=0, atol=1e-12)
+
+
 def test_weights_rows_and_starts(oracle_mod):
     shape, ks = (1, 4, 6, 7, 2, 16), (3, 5, 5)
     q, k, v = make_inputs(shape, seed=7)

@@ -33,6 +33,8 @@ MUTANTS = [
     ("last_dim_dropped", "for (int d = 0; d < HD; ++d)\n          acc +=",
      "for (int d = 0; d < HD - 1; ++d)\n          acc +="),
     ("exp_sign", "e[j] = exp(s[j] - m);", "e[j] = exp(m - s[j]);"),
+    ("weights_reversed", "wts[j] = e[j] / l;", "wts[K - 1 - j] = e[j] / l;"),
+    ("weights_unnormalised", "wts[j] = e[j] / l;", "wts[j] = e[j];"),
 ]
 
 CHECKS = [
@@ -45,6 +47,7 @@ CHECKS = [
     lambda o: pins.test_zero_query_gives_window_mean(o),
     lambda o: pins.test_dominant_key_is_selected(o),
     lambda o: pins.test_window_equal_to_grid_is_dense_attention(o),
+    lambda o: pins.test_weights_match_dense_masked_in_window_order(o),
 ]
 
 

@@ -109,6 +109,53 @@ def test_workload_sampled_full_size(name):
         "output leaves the convex hull of the value rows"
 
 
+def test_large_window_full_grid():
+    """The 11x11x11 workload at its full size, every output against the
+    oracle, in the launch configuration the benchmark times."""
+    w = WORKLOADS["large_window"]
+    full_grid_check(w.shape, w.window, w.seed, "large_window (full grid)", w.k_outlier_frac)
+
+
+def test_full_scale_full_grid_streamed():
+    """The full-scale workload (12.6 M query-heads, HD 128, x8 key outliers),
+    every output against the oracle.  The GPU runs the whole grid once in the
+    benchmark's launch configuration; the oracle (float64) is evaluated one
+    query plane at a time, with windows placed in the whole grid, so host
+    memory stays bounded; errors are accumulated over the whole tensor."""
+    w = WORKLOADS["full_scale"]
+    B, T, H, W, NH, HD = w.shape
+    print("case full_scale (full grid) shape=%s window=%s seed=%d" % (w.shape, w.window, w.seed),
+          flush=True)
+    q, k, v = inputs_on_gpu(w.shape, w.seed, w.k_outlier_frac)
+    out = run(q, k, v, w.window)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    del q, k, v
+    got_all = out.cpu()
+    del out
+    torch.cuda.empty_cache()
+    grid = np.stack(np.meshgrid(np.arange(B), [0], np.arange(H), np.arange(W), np.arange(NH),
+                                indexing="ij"), axis=-1).reshape(-1, 5)
+    sq_diff = sq_ref = 0.0
+    worst = 0.0
+    for t in range(T):
+        pts = grid.copy()
+        pts[:, 1] = t
+        ref = oracle.fwd_points(qc, kc, vc, w.window, pts)
+        got = got_all[:, t].to(torch.float64).numpy().reshape(-1, HD)
+        assert np.isfinite(got).all(), "non-finite output in plane %d" % t
+        d = got - ref
+        sq_diff += float((d * d).sum())
+        sq_ref += float((ref * ref).sum())
+        worst = max(worst, float(np.abs(d).max()))
+        if t % 8 == 7:
+            print("  planes 0..%d: rel_l2 so far %.3e, max_abs %.3e"
+                  % (t, (sq_diff / sq_ref) ** 0.5, worst), flush=True)
+    rel = (sq_diff / sq_ref) ** 0.5
+    print("full_scale (full grid): rel_l2=%.3e max_abs=%.3e" % (rel, worst), flush=True)
+    assert rel <= REL_L2 and worst <= MAX_ABS, (rel, worst)
+    assert rel <= REL_L2_EXPECTED, ("above the derived error level", rel)
+
+
 def test_large_window_reduced_full_grid():
     full_grid_check((1, 12, 20, 24, 2, 64), (11, 11, 11), 41, "11x11x11 reduced grid")
 
@@ -135,7 +182,23 @@ EDGE_CASES = [
     ((1, 4, 8, 128, 2, 64), (3, 5, 27)),       # the pages' 3x5x27 benchmark shape
     ((1, 2, 40, 40, 1, 256), (1, 33, 33)),     # halo larger than LDS: staged in chunks
     ((1, 16, 7, 9, 2, 64), (16, 7, 9)),        # every axis covered
+    # windows wider than 33 along W, and wider than 17 on grids narrower than
+    # 32: the shapes the pages' kernel refused and sent to tiled SDPA (xDiT PR
+    # "LTX-2.5 optimization: integrate faster AITER NA3D flash attention",
+    # Summary, shape gate)
+    ((1, 4, 8, 128, 2, 64), (3, 5, 35)),
+    ((1, 4, 8, 128, 2, 64), (3, 5, 41)),
+    ((1, 4, 16, 31, 2, 64), (3, 7, 27)),
+    ((1, 8, 32, 64, 1, 128), (3, 5, 35)),
+    ((1, 8, 32, 64, 1, 32), (3, 5, 35)),
 ]
+for _hd in (64, 128):
+    for _kw in (35, 41, 63):
+        for _w in (_kw, _kw + 5):
+            EDGE_CASES.append(((1, 4, 8, _w, 2, _hd), (3, 5, _kw)))
+    for _kw in (19, 27):
+        for _w in sorted({_kw, 31}):
+            EDGE_CASES.append(((1, 4, 16, _w, 2, _hd), (3, 7, _kw)))
 
 
 @pytest.mark.parametrize("shape,ks", EDGE_CASES, ids=[str(c) for c in EDGE_CASES])

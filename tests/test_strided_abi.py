@@ -148,3 +148,15 @@ def test_strided_fwd_rejects_before_any_device_call():
 def test_stride_array_shape():
     with pytest.raises(ValueError):
         na._stride_array([(1, 2, 3, 4, 5)] * 3)
+
+
+def test_stride_products_that_overflow_are_rejected():
+    """Strides up to 2^56 times extents up to 2^31 exceed 64 bits: the span
+    and extent arithmetic must report them, not wrap."""
+    shape = (1 << 20, 4, 6, 8, 2, 32)
+    c = contiguous(SHAPE)
+    huge = (1 << 56, c[1], c[2], c[3], c[4])
+    ptrs = (BASE, BASE + (1 << 40), BASE + (2 << 40), BASE + (3 << 40))
+    assert check(ptrs, [huge, c, c, c], shape=shape) == na.NA3D_ERR_STRIDE
+    assert check(ptrs, [c, c, c, huge], shape=shape) == na.NA3D_ERR_STRIDE
+    assert check(ptrs, [c, huge, huge, c], shape=shape) == na.NA3D_ERR_STRIDE
