@@ -33,9 +33,12 @@
 // units run as a software pipeline, so one unit's exponentials share a
 // branch-free region with the next unit's score MFMAs and the previous
 // unit's P.V MFMAs:
-//   S^T = K . Q^T + mask    bf16 MFMA 16x16x32, seeded with the window mask
-//                           (0 or -2^100): one MFMA per tile of the mask,
-//                           kept as bf16 in registers, against the identity
+//   S^T = K . Q^T + mask    bf16 MFMA 16x16x32 whose accumulator starts at the
+//                           window mask (0 or -2^100): a register table that is
+//                           the first MFMA's accumulator input when a wave
+//                           reads at most 7 tiles per plane, else one MFMA
+//                           per tile of masks kept as bf16 pairs against
+//                           the identity
 //   softmax                 one exact max over the group's scores, a
 //                           rescale of the running output only when the max
 //                           rises by more than kRescale, then exp2
@@ -251,6 +254,9 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   constexpr int GK = 16 * NK;      // keys per softmax group
   constexpr int NP = NK / 2;       // 32-key tile pairs per group
   constexpr bool ODD = (NK & 1) != 0;
+  // window masks as an fp32 accumulator-input table (see below) when a wave
+  // reads at most 7 tiles per key plane, else as bf16 pairs applied by MFMA
+  constexpr bool kMaskTable = NG * NK <= 7;
   // V^T operands of all ones (bf16 1.0): the MFMA against P^T sums the
   // weights of each query, already reduced over its four lanes
   const bf16x8 kOnes8 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
@@ -344,8 +350,8 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   }
   const int kp = key_perm(HD, q16);
   constexpr int NKP = (NK + 1) / 2;  // tile pairs per group
-  uint4 mk[NG][NKP];                 // tiles 2p (x, y) and 2p + 1 (z, w)
-  {
+  uint4 mk[kMaskTable ? 1 : NG][NKP];  // tiles 2p (x, y) and 2p + 1 (z, w)
+  if constexpr (!kMaskTable) {
     // halo coordinates of this lane's key row, advanced 16 rows per tile
     int r = rb + kp;
     int uh = r / hwd, uw = r - (r / hwd) * hwd;
@@ -378,6 +384,46 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
           ++uh;
         }
       }
+  }
+  // With few tiles per wave the masks are kept instead in the S^T
+  // accumulator layout, as the accumulator input of each tile's first score
+  // MFMA, so masking costs no instruction per tile: for tile c of group gi,
+  // lane (q16, g) holds query q16 of the block against the keys
+  // key_perm(4g + r) of the tile, r = 0..3, as 0 or -2^100 (fp32).  The
+  // key-to-row map is the same on every key plane, so the table is built once
+  // per wave.  It takes 4 registers per tile (the bf16 pairs above take 2,
+  // plus the identity), so it is used where it leaves the register budget of
+  // the variant intact.
+  f32x4 mc[kMaskTable ? NG : 1][kMaskTable ? NK : 1];
+  if constexpr (kMaskTable) {
+    const int qhm = bh0 + q16 / QW, qwm = w0 + q16 % QW;
+    const bool okm = active && qhm < Hq && qwm < Wq;
+    // window start of this lane's query, relative to the halo
+    const int ahm = okm ? wsh(qhm) - hh0 : -(1 << 20);
+    const int awm = wsw(min(qwm, Wq - 1)) - hw0;
+    const float kMaskF = __builtin_bit_cast(float, kMaskBits << 16);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // halo coordinates of key row key_perm(4g + r), advanced 16 rows per tile
+      int row = rb + key_perm(HD, 4 * g + r);
+      int uh = row / hwd, uw = row - (row / hwd) * hwd;
+      const int dh = 16 / hwd, dw = 16 % hwd;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int c = 0; c < NK; ++c) {
+          const bool in = row < halo_rows && (unsigned)(uh - ahm) < (unsigned)KH &&
+                          (unsigned)(uw - awm) < (unsigned)KW;
+          mc[gi][c][r] = in ? 0.f : kMaskF;
+          row += 16;
+          uh += dh;
+          uw += dw;
+          if (uw >= hwd) {
+            uw -= hwd;
+            ++uh;
+          }
+        }
+    }
   }
   // B operands of the mask MFMA (16x16x32): lane (q16, g) holds rows
   // 8g .. 8g+7 of column q16.  Row 8g + i carries query 4g + (i & 3) of the
@@ -624,14 +670,21 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
               kf[ks] = (32 * ks + 8 * g < HD)
                            ? *reinterpret_cast<const bf16x8*>(lk + kofs[ks] + gofs + 16 * c * RB)
                            : bf16x8{};
-            // the window mask of tile c: the pair's mask against the identity
-            // half that selects tile c (same MFMA kind as the score chain,
-            // whose accumulator it seeds)
-            out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, mk[gi][c >> 1]), (c & 1) ? ident_o : ident_e,
-                f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            if constexpr (kMaskTable) {
+              // the window mask of tile c is the accumulator input of the chain
+              out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], S[sl].qf[0],
+                                                               mc[gi][c], 0, 0, 0);
+            } else {
+              // the window mask of tile c: the pair's mask against the identity
+              // half that selects tile c (same MFMA kind as the score chain,
+              // whose accumulator it seeds)
+              out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, mk[gi][c >> 1]), (c & 1) ? ident_o : ident_e,
+                  f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+              out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], S[sl].qf[0], out[c], 0, 0, 0);
+            }
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks)
+            for (int ks = 1; ks < KSTEPS; ++ks)
               out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], S[sl].qf[ks], out[c], 0, 0, 0);
           }
         };
