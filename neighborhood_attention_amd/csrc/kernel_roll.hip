@@ -662,30 +662,67 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
         auto unit_scores = [&](int u, f32x4 (&out)[NK]) __attribute__((always_inline)) {
           const int gi = u / NS, sl = u % NS;
           const int gofs = GK * gi * RB;
-#pragma unroll
-          for (int c = 0; c < NK; ++c) {
-            bf16x8 kf[KSTEPS];
+          auto load_k = [&](int c, bf16x8 (&kf)[KSTEPS]) __attribute__((always_inline)) {
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks)
               kf[ks] = (32 * ks + 8 * g < HD)
                            ? *reinterpret_cast<const bf16x8*>(lk + kofs[ks] + gofs + 16 * c * RB)
                            : bf16x8{};
-            if constexpr (kMaskTable) {
-              // the window mask of tile c is the accumulator input of the chain
-              out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], S[sl].qf[0],
-                                                               mc[gi][c], 0, 0, 0);
-            } else {
-              // the window mask of tile c: the pair's mask against the identity
-              // half that selects tile c (same MFMA kind as the score chain,
-              // whose accumulator it seeds)
-              out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8, mk[gi][c >> 1]), (c & 1) ? ident_o : ident_e,
-                  f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-              out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], S[sl].qf[0], out[c], 0, 0, 0);
-            }
+          };
+          // The chains of two tiles at a time, interleaved, so one tile's
+          // dependent MFMA never waits directly on the previous one; one tile
+          // at a time where a second K fragment set would not fit the register
+          // cap of the variant.
+          constexpr int kPair = (OCC > 0 && NG > 1) ? 1 : 2;
+          if constexpr (kPair == 1) {
 #pragma unroll
-            for (int ks = 1; ks < KSTEPS; ++ks)
-              out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], S[sl].qf[ks], out[c], 0, 0, 0);
+            for (int c = 0; c < NK; ++c) {
+              bf16x8 kf[KSTEPS];
+              load_k(c, kf);
+              if constexpr (kMaskTable) {
+                out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], S[sl].qf[0], mc[gi][c], 0, 0, 0);
+              } else {
+                out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, mk[gi][c >> 1]), (c & 1) ? ident_o : ident_e,
+                    f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], S[sl].qf[0], out[c], 0, 0, 0);
+              }
+#pragma unroll
+              for (int ks = 1; ks < KSTEPS; ++ks)
+                out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], S[sl].qf[ks], out[c], 0, 0, 0);
+            }
+          } else {
+#pragma unroll
+            for (int c0 = 0; c0 < NK; c0 += kPair) {
+              bf16x8 kf[kPair][KSTEPS];
+#pragma unroll
+              for (int t = 0; t < kPair; ++t)
+                if (c0 + t < NK) load_k(c0 + t, kf[t]);
+              if constexpr (!kMaskTable) {
+                // the window mask of tile c: the pair's mask against the
+                // identity half that selects tile c (same MFMA kind as the
+                // score chain, whose accumulator it seeds)
+#pragma unroll
+                for (int t = 0; t < kPair; ++t)
+                  if (c0 + t < NK)
+                    out[c0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, mk[gi][(c0 + t) >> 1]),
+                        ((c0 + t) & 1) ? ident_o : ident_e, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+              }
+#pragma unroll
+              for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+                for (int t = 0; t < kPair; ++t) {
+                  const int c = c0 + t;
+                  if (c >= NK) continue;
+                  f32x4 acc_in;
+                  if constexpr (kMaskTable)
+                    acc_in = ks == 0 ? mc[gi][c] : out[c];
+                  else
+                    acc_in = out[c];
+                  out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][ks], S[sl].qf[ks], acc_in, 0, 0, 0);
+                }
+            }
           }
         };
         // max of unit u's scores; the reference max moves (and the running
