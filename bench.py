@@ -528,31 +528,34 @@ def cpu_model():
 
 
 def gpu_clocks():
-    """Current shader / memory clocks as the SMI tools report them (MHz), or
-    the reason they are not available."""
+    """Shader and memory clocks as amd-smi reports them for GPU 0 (MHz): the
+    current value (sampled right after a timed region, so the GPU is still
+    clocked up), the maximum, and whether the clock is locked; or the reason
+    they are not available."""
     import subprocess
 
-    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
-        try:
-            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
-        except (OSError, subprocess.TimeoutExpired) as e:
-            last = "%s: %s" % (cmd[0], type(e).__name__)
-            continue
-        if r.returncode != 0:
-            last = "%s: exit %d" % (cmd[0], r.returncode)
-            continue
-        txt = r.stdout
-        found = {}
-        for key, pat in (("sclk_MHz", r'"(?:gfx_0|gfx|sclk)[^"]*"[^{}]*?"clk"\s*:\s*\{?[^}]*?"value"\s*:\s*(\d+)'),
-                         ("mclk_MHz", r'"(?:mem_0|mem|mclk)[^"]*"[^{}]*?"clk"\s*:\s*\{?[^}]*?"value"\s*:\s*(\d+)'),
-                         ("sclk_MHz", r'sclk[^"]*"\s*:\s*"\(?(\d+)\s*Mhz'),
-                         ("mclk_MHz", r'mclk[^"]*"\s*:\s*"\(?(\d+)\s*Mhz')):
-            m = re.search(pat, txt, re.I | re.S)
-            if m and key not in found:
-                found[key] = int(m.group(1))
-        found["source"] = " ".join(cmd)
-        return found
-    return {"source": "unavailable (%s)" % last}
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        data = json.loads(r.stdout[r.stdout.index("{"):]) if r.returncode == 0 else None
+    except (OSError, subprocess.TimeoutExpired, ValueError) as e:
+        return {"source": "amd-smi unavailable (%s)" % type(e).__name__}
+    if data is None:
+        return {"source": "amd-smi exit %d" % r.returncode}
+    try:
+        clk = data["gpu_data"][0]["clock"]
+        out = {"source": "amd-smi metric --clock"}
+        for key, name in (("gfx_0", "sclk"), ("mem_0", "mclk")):
+            c = clk.get(key) or {}
+            for field in ("clk", "max_clk"):
+                v = (c.get(field) or {}).get("value")
+                if isinstance(v, (int, float)):
+                    out["%s_%s_MHz" % (name, field.replace("_clk", "").replace("clk", "cur"))] = v
+            if "clk_locked" in c:
+                out["%s_locked" % name] = c["clk_locked"]
+        return out
+    except (KeyError, IndexError, TypeError, AttributeError):
+        return {"source": "amd-smi output not understood"}
 
 
 def provenance():
@@ -562,7 +565,6 @@ def provenance():
         "torch": torch.__version__, "hip": torch.version.hip,
         "gpu": torch.cuda.get_device_name(0),
         "cpu_model": cpu_model(), "host_threads": len(os.sched_getaffinity(0)),
-        "clocks": gpu_clocks(),
     }
 
 
@@ -645,6 +647,7 @@ def main():
     rec = bench_workload(args.workload, args.steps, args.warmup, check=not args.no_check,
                          cpu=not args.no_cpu_baseline, cpu_s=args.cpu_seconds,
                          cold=not args.no_cold)
+    clocks = gpu_clocks()  # right after the headline's timed launches
     if args.workload == HEADLINE and not args.no_large_window:
         # the metric also names the 11x11x11 window: report it beside the headline
         lw = bench_workload("large_window", args.steps, args.warmup, check=not args.no_check,
@@ -663,6 +666,8 @@ def main():
             "shape_BTHWNH_HD": ww["config"]["shape_BTHWNH_HD"], "value": ww["value"],
             "unit": "TFLOP/s", "kernel_us": ww["kernel_us"], "roofline": ww["roofline"],
             "parity_sampled": ww["parity_sampled"], "variant": ww["config"]["variant"]}
+        # a window wider than 33 along W (the shapes the pages' kernel refused)
+        rec["wide_window_3x5x41"] = companion("wide_w41", args.steps, args.warmup)
     if args.workload == HEADLINE and not args.no_configs:
         # the remaining workloads of the metric's configuration list, each with
         # its own roofline: full scale (HD 128, x8 key outliers; fewer
@@ -682,12 +687,14 @@ def main():
         # reach here, beside the specification peaks
         meas = {"hbm": rec["measured_copy_GBps"], "mfma": rec["measured_gemm_TFLOPs"]}
         for sub in [rec] + [rec[k] for k in ("large_window_11x11x11", "wide_window_3x5x27",
-                                             "full_scale", "narrow_w7", "narrow_w5", "tiny")
+                                             "wide_window_3x5x41", "full_scale", "narrow_w7",
+                                             "narrow_w5", "tiny")
                             if k in rec]:
             rf = sub["roofline"]
             rf["measured_peak"] = meas[rf["bound"]]
             rf["frac_of_measured_peak"] = round(rf["achieved"] / meas[rf["bound"]], 4)
         rec["provenance"] = provenance()
+        rec["provenance"]["clocks"] = clocks
     if args.workload == HEADLINE and not args.no_batch:
         rec["decoder_tiles_batched"] = bench_batch(args.steps, args.warmup)
     if args.workload == HEADLINE and not args.no_rms_norm:

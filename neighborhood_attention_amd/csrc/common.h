@@ -167,7 +167,12 @@ struct Launch {
   X(50, 64, 2, 8, 2, 4, 1, 13, 1, 1, 0) \
   X(51, 64, 2, 8, 2, 4, 1, 13, 1, 2, 0) \
   X(52, 256, 2, 8, 1, 4, 1, 7, 1, 1, 0) \
-  X(53, 256, 4, 4, 1, 4, 1, 7, 1, 1, 0)
+  X(53, 256, 4, 4, 1, 4, 1, 7, 1, 1, 0) \
+  X(54, 64, 2, 8, 2, 4, 1, 9, 2, 1, 0) \
+  X(55, 64, 2, 8, 2, 4, 1, 7, 3, 1, 0) \
+  X(56, 64, 2, 8, 2, 4, 1, 7, 4, 1, 0) \
+  X(57, 128, 2, 8, 1, 4, 1, 9, 2, 1, 0) \
+  X(58, 64, 2, 8, 1, 4, 1, 9, 2, 1, 0)
 
 struct RollVariant {
   int hd, qh, qw, wh, wt, ns, nk, ng, nbuf, occ;

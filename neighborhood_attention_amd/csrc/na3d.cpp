@@ -280,9 +280,13 @@ int pick_roll(const Geom& g, Launch* l) {
   static const int p64_small[] = {8, 34, 21, 26, 20, 9};       // union <= 64 keys
   static const int p64_mid[] = {42, 43, 40, 38, 35, 26, 34, 21, 20, 1, 9, 10};  // <= 112 keys
   // larger windows: 4x4 blocks for near-cubic ones; 2x8 blocks for windows
-  // much wider along W (their union is smaller in 2x8 blocks)
-  static const int p64_large[] = {5, 46, 51, 50, 49, 10, 22, 6, 7, 9};
-  static const int p128[] = {47, 25, 15, 14, 13, 16, 29};
+  // much wider along W (their union is smaller in 2x8 blocks), with one
+  // 13-tile group up to a 208-key union and two to four groups beyond (the
+  // windows wider than 33 that the pages' kernel refused: measured 1.9-2.8x
+  // faster than the 4x4 two-group variant 10 and 3.5x faster than the
+  // general family on (3,5,35) to (3,5,63))
+  static const int p64_large[] = {5, 46, 51, 50, 49, 58, 55, 56, 10, 22, 6, 7, 9};
+  static const int p128[] = {47, 25, 57, 15, 14, 13, 16, 29};
   // head dim 256: one-buffer variants (a two-buffer plane of 512-byte rows
   // does not fit LDS; measured 548 us against 862 us for the general family
   // on 16x64x96, 4 heads, (3,7,7))

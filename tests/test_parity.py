@@ -69,7 +69,8 @@ def _gpu_ready():
 
 
 # ------------------------------------------------------------ workloads
-@pytest.mark.parametrize("name", ["tiny", "narrow_w7", "narrow_w5", "decoder_tile", "wide_w27"])
+@pytest.mark.parametrize("name", ["tiny", "narrow_w7", "narrow_w5", "decoder_tile", "wide_w27",
+                                  "wide_w41"])
 def test_workload_full_grid(name):
     w = WORKLOADS[name]
     full_grid_check(w.shape, w.window, w.seed, name, w.k_outlier_frac)
