@@ -146,25 +146,57 @@ __device__ __forceinline__ void reset_state(Slot<HD>& S) {
   S.m = kNegInf;
 }
 
-// Normalised output of a retired query plane, packed as bf16 (RNE) for the
-// 8-byte stores of lane (q16, g): head dims 16mt + 4g .. +3.
+__device__ __forceinline__ void swap16u(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32u(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// Normalised output of a retired query plane, packed as bf16 (RNE).  Lane
+// (q16, g) holds head dims 16mt + 4g .. +3 (8 bytes) of query q16 for each mt.
+// For HD >= 32 the 8-byte pieces of each pair of tiles (2j, 2j+1) are then
+// regrouped among the four lanes of the query (lane groups g, all exchanges
+// stay within one query) so that lane g holds head dims 32j + 8g .. +7: each
+// 16-byte store then writes 64 contiguous bytes of every query row (half as
+// many store instructions, whole 64-byte segments instead of 32-byte ones).
+// Start: group g holds A = piece (g, 2j), B = piece (g, 2j+1).  The 32-lane
+// swap exchanges groups {2,3} of A with groups {0,1} of B; the 16-lane swap
+// then exchanges group 1 of A with group 0 of B and group 3 of A with group 2
+// of B, leaving group g with the pieces at dims 32j + 8g and 32j + 8g + 4.
 template <int HD>
 __device__ __forceinline__ void pack_out(const Slot<HD>& S, uint32_t (&pk)[2 * Slot<HD>::MT]) {
+  constexpr int MT = Slot<HD>::MT;
   const float inv = 1.f / S.accl[0];
 #pragma unroll
-  for (int mt = 0; mt < Slot<HD>::MT; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     const bf16x2 lo = {(__bf16)(S.acc[mt][0] * inv), (__bf16)(S.acc[mt][1] * inv)};
     const bf16x2 hi = {(__bf16)(S.acc[mt][2] * inv), (__bf16)(S.acc[mt][3] * inv)};
     pk[2 * mt] = __builtin_bit_cast(uint32_t, lo);
     pk[2 * mt + 1] = __builtin_bit_cast(uint32_t, hi);
   }
+  if constexpr (MT >= 2) {
+#pragma unroll
+    for (int j = 0; j < MT / 2; ++j) {
+      swap32u(pk[4 * j], pk[4 * j + 2]);
+      swap32u(pk[4 * j + 1], pk[4 * j + 3]);
+      swap16u(pk[4 * j], pk[4 * j + 2]);
+      swap16u(pk[4 * j + 1], pk[4 * j + 3]);
+    }
+  }
 }
 
+// Stores of a packed output (layout of pack_out).
 template <int MT>
 __device__ __forceinline__ void store_out(uint16_t* op, const uint32_t (&pk)[2 * MT], int g) {
+  if constexpr (MT >= 2) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    *reinterpret_cast<uint2*>(op + 16 * mt + 4 * g) = make_uint2(pk[2 * mt], pk[2 * mt + 1]);
+    for (int j = 0; j < MT / 2; ++j)
+      *reinterpret_cast<uint4*>(op + 32 * j + 8 * g) =
+          make_uint4(pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]);
+  } else {
+    *reinterpret_cast<uint2*>(op + 4 * g) = make_uint2(pk[0], pk[1]);
+  }
 }
 
 // V^T operand through the transpose read: lane (4j + a) of a 16-lane group
