@@ -105,6 +105,7 @@ struct Launch {
   int lds_rows;    // rows of each K and V staging buffer
   int lds_bytes;
   int planes;      // K/V planes staged per workgroup (maximum)
+  int band_h;      // rolling: tile rows per band of the spatial visiting order
 };
 
 // Instantiations of the rolling family: index, head dim, query block

@@ -92,6 +92,7 @@ struct RollArgs {
   int nruns;     // runs along T
   int rpw;       // consecutive runs streamed by one workgroup
   int lds_rows;  // rows of each K and V staging buffer
+  int band_h;    // spatial tiles are visited in bands of this many tile rows
   Strides sq, sk, sv, so;  // element strides; k and v share h, w and n
 };
 
@@ -308,13 +309,23 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   const int ih = wave % WH;
   const int it = wave / WH;
 
-  // ---- workgroup -> (b, n, tile_h, tile_w, run group); run groups vary fastest
+  // ---- workgroup -> (b, n, tile_h, tile_w, run group); run groups vary
+  // fastest.  Within a head the spatial tiles are visited in bands of band_h
+  // tile rows, down each band's column of tiles before the next column, so
+  // the workgroups in flight on one XCD (consecutive indices, see xcd_remap)
+  // cover a compact block of the grid and read the halo rows they share
+  // from that XCD's L2 rather than from HBM.
   const int tt = wg % a.tiles_t;
   wg /= a.tiles_t;
-  const int tw = wg % a.tiles_w;
-  wg /= a.tiles_w;
-  const int th = wg % a.tiles_h;
-  wg /= a.tiles_h;
+  const int ntile = a.tiles_h * a.tiles_w;
+  const int j = wg % ntile;
+  wg /= ntile;
+  const int band_rows = a.band_h * a.tiles_w;
+  const int band = j / band_rows;
+  const int jb = j - band * band_rows;
+  const int gh = min(a.band_h, a.tiles_h - band * a.band_h);  // rows in this band
+  const int th = band * a.band_h + jb % gh;
+  const int tw = jb / gh;
   const int n = wg % a.NH;
   const int b = wg / a.NH;
 
@@ -894,6 +905,7 @@ na3d_fwd_roll_batch_kernel(const RollArgs shared, const RollBatch bt) {
   a.tiles_t = t.tiles_t; a.tiles_h = t.tiles_h; a.tiles_w = t.tiles_w;
   a.tc = t.tc; a.ta = t.ta; a.tz = t.tz; a.nruns = t.nruns; a.rpw = t.rpw;
   a.lds_rows = t.lds_rows;
+  a.band_h = 1;
   Strides c;
   c.n = HD;
   c.w = (int64_t)a.NH * HD;
@@ -939,6 +951,7 @@ int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s) {
   a.nruns = l.nruns;
   a.rpw = l.rpw;
   a.lds_rows = l.lds_rows;
+  a.band_h = l.band_h;
   a.sq = p.sq;
   a.sk = p.sk;
   a.sv = p.sv;
@@ -966,6 +979,7 @@ int launch_roll_batch(const Problem& p, const Launch& l, const RollBatch& bt, in
   a.tiles_t = a.tiles_h = a.tiles_w = 0;
   a.tc = a.ta = a.tz = a.nruns = a.rpw = 0;
   a.lds_rows = l.lds_rows;
+  a.band_h = 1;
   a.sq = a.sk = a.sv = a.so = Strides{0, 0, 0, 0, 0};
   if (l.variant < 0 || l.variant >= kNumRollVariants || kRollVariants[l.variant].hd != hd) return -1;
   if (bt.n < 1 || bt.n > kMaxBatch) return -1;

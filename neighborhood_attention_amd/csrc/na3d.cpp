@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -205,6 +206,7 @@ bool plan_general(const Geom& g, Launch* l) {
   l->lds_rows = std::min(max_halo, kGeneralLdsBytes / (2 * row));
   l->lds_bytes = 2 * l->lds_rows * row;
   l->planes = g.KT;
+  l->band_h = 1;
   return l->wgs <= 0x7fffffff;
 }
 
@@ -268,6 +270,16 @@ bool plan_roll(int v, const Geom& g, int tile_t, Launch* l, int target = kTarget
   l->lds_rows = rows;
   l->lds_bytes = (int)lds;
   l->planes = std::min(rpw, nruns) == 1 ? most : total;  // upper bound for run groups
+  // Visiting order of the spatial tiles: bands of band_h tile rows, so that
+  // the tiles in flight on one XCD (32 CUs, as many workgroups per CU as LDS
+  // allows, consecutive workgroup indices) form a block about as tall as it
+  // is wide in query space and share their halo rows in that XCD's L2.
+  {
+    const int per_cu = std::max(1, kMaxLdsBytes / std::max(1, l->lds_bytes));
+    const double tiles_in_flight = 32.0 * per_cu / l->tiles_t;
+    const double bh = std::sqrt(tiles_in_flight * rv.qw / BH);
+    l->band_h = std::max(1, std::min(tiles_h, (int)std::lround(bh)));
+  }
   return l->wgs <= 0x7fffffff;
 }
 
