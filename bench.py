@@ -296,6 +296,7 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0, cold=T
             "shape_BTHWNH_HD": list(w.shape),
             "window": list(w.window),
             "seed": w.seed,
+            "family": "rolling" if plan["family"] == 2 else "general",
             "variant": plan["variant"],
             "tile": [plan["tile_t"], plan["tile_h"], plan["tile_w"]],
             "workgroups": plan["workgroups"],
@@ -335,7 +336,8 @@ def companion(name, steps, warmup, cold=False):
                                 "kernel_us_graph", "per_launch_us", "roofline", "parity_sampled",
                                 "inputs_sha256")} | {
         "shape_BTHWNH_HD": rec["config"]["shape_BTHWNH_HD"], "window": rec["config"]["window"],
-        "variant": rec["config"]["variant"], "workgroups": rec["config"]["workgroups"]}
+        "family": rec["config"]["family"], "variant": rec["config"]["variant"],
+        "workgroups": rec["config"]["workgroups"]}
 
 
 def bench_fused(name, steps, warmup):
@@ -707,6 +709,10 @@ def main():
             "parity_sampled": ww["parity_sampled"], "variant": ww["config"]["variant"]}
         # a window wider than 33 along W (the shapes the pages' kernel refused)
         rec["wide_window_3x5x41"] = companion("wide_w41", args.steps, args.warmup)
+        # the slowest path: a 19x19x19 window, whose union no rolling
+        # instantiation holds, runs on the general family (~2 ms a launch)
+        rec["general_family_19x19x19"] = companion("window_19", max(3, min(args.steps, 10)),
+                                                   min(args.warmup, 2))
     if args.workload == HEADLINE and not args.no_configs:
         # the remaining workloads of the metric's configuration list, each with
         # its own roofline: full scale (HD 128, x8 key outliers; fewer
@@ -726,8 +732,8 @@ def main():
         # reach here, beside the specification peaks
         meas = {"hbm": rec["measured_copy_GBps"], "mfma": rec["measured_gemm_TFLOPs"]}
         for sub in [rec] + [rec[k] for k in ("large_window_11x11x11", "wide_window_3x5x27",
-                                             "wide_window_3x5x41", "full_scale", "narrow_w7",
-                                             "narrow_w5", "tiny")
+                                             "wide_window_3x5x41", "general_family_19x19x19",
+                                             "full_scale", "narrow_w7", "narrow_w5", "tiny")
                             if k in rec]:
             rf = sub["roofline"]
             rf["measured_peak"] = meas[rf["bound"]]

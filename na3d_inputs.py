@@ -81,6 +81,9 @@ WORKLOADS = {
         Workload("wide_w27", (1, 4, 8, 128, 8, 64), (3, 5, 27), 6,
                  note="anisotropic wide window; grid of the aiter PR's (3,5,27) "
                       "benchmark row (its head count is not stated; 8 here)"),
+        Workload("window_19", (1, 24, 32, 32, 4, 64), (19, 19, 19), 8,
+                 note="a window whose union exceeds every rolling instantiation: the "
+                      "general family's case"),
         Workload("wide_w41", (1, 4, 8, 128, 8, 64), (3, 5, 41), 7,
                  note="a window wider than 33 along W (the Triton kernel's shape gate "
                       "sent these to tiled SDPA) on the same grid"),

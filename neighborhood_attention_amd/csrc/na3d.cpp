@@ -298,7 +298,11 @@ int pick_roll(const Geom& g, Launch* l) {
   // faster than the 4x4 two-group variant 10 and 3.5x faster than the
   // general family on (3,5,35) to (3,5,63))
   static const int p64_large[] = {5, 46, 51, 50, 49, 58, 55, 56, 10, 22, 6, 7, 9};
-  static const int p128[] = {47, 25, 57, 15, 14, 13, 16, 29};
+  // head dim 128: 4x4 blocks (one 13-tile group) before the 2x8 two-group
+  // variants for near-cubic windows (11x11x11 on 16x48x64, 8 heads: 1018 us
+  // against 1299 us for variant 57 and 1632 us for variant 15); the 9-tile
+  // two-group 2x8 variant for wide windows (3x7x19: 1004 us against 1080 us)
+  static const int p128[] = {47, 25, 16, 57, 15, 14, 13, 29};
   // head dim 256: one-buffer variants (a two-buffer plane of 512-byte rows
   // does not fit LDS; measured 548 us against 862 us for the general family
   // on 16x64x96, 4 heads, (3,7,7))

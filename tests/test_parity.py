@@ -117,6 +117,14 @@ def test_large_window_full_grid():
     full_grid_check(w.shape, w.window, w.seed, "large_window (full grid)", w.k_outlier_frac)
 
 
+def test_general_family_workload_full_grid():
+    """The 19x19x19 workload (the general family's case: no rolling
+    instantiation holds its window union) at full size, every output."""
+    w = WORKLOADS["window_19"]
+    assert na.plan(w.shape, w.window)["family"] == 1
+    full_grid_check(w.shape, w.window, w.seed, "window_19 (full grid)", w.k_outlier_frac)
+
+
 def test_full_scale_full_grid_streamed():
     """The full-scale workload (12.6 M query-heads, HD 128, x8 key outliers),
     every output against the oracle.  The GPU runs the whole grid once in the
