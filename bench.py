@@ -92,6 +92,8 @@ def measured_traffic(workload, profile="na3d_fwd_roll_%s_traffic.md", sources=KE
     """HBM bytes per launch from the committed counter summary of this
     workload, if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", profile % workload)
+    if not os.path.exists(path) and "_roll_" in profile:
+        path = os.path.join(ROOT, "profiles", profile.replace("_roll_", "_general_") % workload)
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -127,9 +129,10 @@ def time_kernel(fn, steps, warmup):
 def time_graph(fn, steps):
     """Kernel ms per launch with `steps` launches captured in one HIP graph and
     replayed on the current stream, timed with HIP events on that stream: the
-    kernels run back to back with no host launch gaps between them, which is
-    what makes short kernels measurable (a launch from Python takes longer
-    to issue than a 10-20 us kernel takes to run)."""
+    kernels run back to back with no host launch gaps between them, which
+    shows the duration of kernels shorter than the host's launch interval
+    (a launch from Python takes longer to issue than a 10-20 us kernel takes
+    to run)."""
     import torch
 
     side = torch.cuda.Stream()
@@ -262,10 +265,11 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0, cold=T
         single["cold"] = per_launch_us(fn, max(steps // 2, 5), cold_bytes=512 << 20)
         single["cold"]["between_launches"] = "512 MiB written, GPU drained"
     tflops = w.flops / (wall_ms * 1e-3) / 1e12
-    # the roofline is that of the kernel: its duration from back-to-back
-    # launches replayed from a graph (equal to the eager loop's for kernels
-    # longer than the host's launch interval, free of launch gaps below it)
-    kern_s = graph_ms * 1e-3
+    # the roofline is that of the kernel's duration over the timed region
+    # (HIP events on the launch stream); the graph replay is reported beside
+    # it, since for kernels shorter than the host's launch interval the eager
+    # loop includes launch gaps
+    kern_s = kern_ms * 1e-3
     ai = w.flops / w.bytes
     bound = "mfma" if ai > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
     if bound == "hbm":
@@ -567,34 +571,42 @@ def cpu_model():
 
 
 def gpu_clocks():
-    """Shader and memory clocks as amd-smi reports them for GPU 0 (MHz): the
-    current value (sampled right after a timed region, so the GPU is still
-    clocked up), the maximum, and whether the clock is locked; or the reason
-    they are not available."""
-    import subprocess
+    """Shader and memory clocks of the GPU as the amdgpu driver reports them
+    in sysfs (read as plain files: no other program is started from this
+    GPU-using process): the DPM levels with the current one marked, and
+    the hwmon frequency readings (MHz); sampled right after a timed region,
+    so the GPU is still clocked up.  Empty where the files are not there."""
+    import glob
 
-    try:
-        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
-                           text=True, timeout=20)
-        data = json.loads(r.stdout[r.stdout.index("{"):]) if r.returncode == 0 else None
-    except (OSError, subprocess.TimeoutExpired, ValueError) as e:
-        return {"source": "amd-smi unavailable (%s)" % type(e).__name__}
-    if data is None:
-        return {"source": "amd-smi exit %d" % r.returncode}
-    try:
-        clk = data["gpu_data"][0]["clock"]
-        out = {"source": "amd-smi metric --clock"}
-        for key, name in (("gfx_0", "sclk"), ("mem_0", "mclk")):
-            c = clk.get(key) or {}
-            for field in ("clk", "max_clk"):
-                v = (c.get(field) or {}).get("value")
-                if isinstance(v, (int, float)):
-                    out["%s_%s_MHz" % (name, field.replace("_clk", "").replace("clk", "cur"))] = v
-            if "clk_locked" in c:
-                out["%s_locked" % name] = c["clk_locked"]
-        return out
-    except (KeyError, IndexError, TypeError, AttributeError):
-        return {"source": "amd-smi output not understood"}
+    out = {"source": "sysfs (amdgpu)"}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        found = {}
+        for name, key in (("pp_dpm_sclk", "sclk_levels"), ("pp_dpm_mclk", "mclk_levels")):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    txt = f.read()
+            except OSError:
+                continue
+            levels = [ln.strip() for ln in txt.splitlines() if ln.strip()]
+            found[key] = levels[:16]
+            cur = [ln for ln in levels if ln.endswith("*")]
+            if cur:
+                m = re.search(r"(\d+)\s*[Mm]hz", cur[0])
+                if m:
+                    found[key.replace("levels", "cur_MHz")] = int(m.group(1))
+        for hw in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+            for i in (1, 2):
+                try:
+                    with open(os.path.join(hw, "freq%d_label" % i)) as f:
+                        label = f.read().strip()
+                    with open(os.path.join(hw, "freq%d_input" % i)) as f:
+                        found["%s_MHz" % label] = int(f.read().strip()) // 1000000
+                except (OSError, ValueError):
+                    continue
+        if found:
+            out[os.path.basename(os.path.dirname(dev))] = found
+            break
+    return out
 
 
 def provenance():
