@@ -146,6 +146,26 @@ def make_inputs(shape, seed: int, device="cpu", k_outlier_frac: float = 0.0,
     return q, k, v
 
 
+def make_spike_inputs(shape, seed: int, spikes, device="cpu"):
+    """(q, k, v) whose scores hold a few extreme keys: q is ones/HD plus a
+    little noise, k and v are standard normal, and for every (t, h, w, s) in
+    ``spikes`` the key at that grid position (all batches and heads) is the
+    constant s, so its score is about s (and s*(1 +- 0.25) across queries)
+    against scores of about +-0.2 elsewhere."""
+    shape = tuple(int(x) for x in shape)
+    hd = shape[-1]
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed))
+    q = (1.0 / hd + torch.randn(shape, generator=g, device=dev) * (0.25 / hd ** 0.5)).to(torch.bfloat16)
+    k = torch.randn(shape, generator=g, device=dev)
+    for (t, h, w, s) in spikes:
+        k[:, t, h, w] = float(s)
+    k = k.to(torch.bfloat16)
+    v = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+    return q, k, v
+
+
 def workload_inputs(name: str, device="cpu"):
     w = WORKLOADS[name]
     return make_inputs(w.shape, w.seed, device, w.k_outlier_frac, w.k_outlier_scale)

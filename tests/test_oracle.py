@@ -245,6 +245,29 @@ def test_dominant_key_is_selected(oracle_mod):
                                rtol=0, atol=1e-12 + 1e-15 * 97 * 27)
 
 
+def test_extreme_scores_stay_finite(oracle_mod):
+    """Keys with scores of +-1000 (exp of them overflows or underflows any
+    float format without the max subtracted): every output stays finite and
+    matches the dense masked softmax, and a query whose window holds the +1000
+    key returns that key's v exactly (every other weight is e^-1000 = 0)."""
+    from na3d_inputs import make_spike_inputs
+    shape, ks = (1, 4, 6, 7, 2, 16), (3, 3, 5)
+    spike = (1, 2, 3)
+    q, k, v = make_spike_inputs(shape, 5, [spike + (1000,), (3, 5, 6, -1000)])
+    got = oracle_mod.fwd(q, k, v, ks)
+    assert np.isfinite(got).all()
+    ref, M = dense_masked(q, k, v, ks)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    T, H, W = shape[1:4]
+    sid = (spike[0] * H + spike[1]) * W + spike[2]
+    hits = 0
+    for t, h, w in itertools.product(range(T), range(H), range(W)):
+        if M[(t * H + h) * W + w, sid]:
+            np.testing.assert_array_equal(got[0, t, h, w], f64(v)[0, spike[0], spike[1], spike[2]])
+            hits += 1
+    assert 0 < hits < T * H * W
+
+
 # ---------------------------------------------------------------- invariants
 @pytest.mark.parametrize("axis", [1, 2, 3])
 def test_flip_equivariance_odd_window(oracle_mod, axis):

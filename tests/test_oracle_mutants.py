@@ -33,6 +33,7 @@ MUTANTS = [
     ("last_dim_dropped", "for (int d = 0; d < HD; ++d)\n          acc +=",
      "for (int d = 0; d < HD - 1; ++d)\n          acc +="),
     ("exp_sign", "e[j] = exp(s[j] - m);", "e[j] = exp(m - s[j]);"),
+    ("max_not_subtracted", "e[j] = exp(s[j] - m);", "e[j] = exp(s[j]);"),
     ("weights_reversed", "wts[j] = e[j] / l;", "wts[K - 1 - j] = e[j] / l;"),
     ("weights_unnormalised", "wts[j] = e[j] / l;", "wts[j] = e[j];"),
 ]
@@ -48,6 +49,7 @@ CHECKS = [
     lambda o: pins.test_dominant_key_is_selected(o),
     lambda o: pins.test_window_equal_to_grid_is_dense_attention(o),
     lambda o: pins.test_weights_match_dense_masked_in_window_order(o),
+    lambda o: pins.test_extreme_scores_stay_finite(o),
 ]
 
 

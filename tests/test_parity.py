@@ -319,3 +319,61 @@ def test_rolling_run_lengths(tile_t):
     out = na.fwd(q, k, v, ks, config=(2, p["variant"], tile_t))
     torch.cuda.synchronize()
     compare(to_np(out), oracle.fwd(q.cpu(), k.cpu(), v.cpu(), ks), "run length %d" % tile_t)
+
+
+# ------------------------------------------------------------ extreme scores
+# A few keys whose scores stand far above (or below) the rest, on grids of
+# every kernel class (4x4 and 2x8 blocks with 13-tile unions, mask-table
+# variants, two-group wide windows): a later key plane that raises a query's
+# running max by 30 to 250 (the running output is rescaled by e^-30 ... e^-250,
+# far below bf16's smallest normal), first key planes whose window union but
+# not the query's own window holds such a key (it must not enter that query's
+# max), and keys far below every other score.  The oracle subtracts the exact
+# max in fp64.
+SPIKE_CASES = [
+    ((1, 12, 20, 24, 2, 64), (11, 11, 11),
+     [(0, 0, 0, 100), (6, 10, 12, 40), (11, 19, 23, -100), (3, 15, 5, 200), (9, 2, 20, 30)]),
+    ((1, 12, 20, 24, 1, 128), (11, 11, 11),
+     [(0, 0, 0, 100), (6, 10, 12, 40), (3, 15, 5, 200), (9, 2, 20, 30)]),
+    ((1, 6, 8, 128, 2, 64), (3, 5, 27),
+     [(0, 0, 0, 100), (2, 4, 60, 40), (5, 7, 127, 200), (3, 1, 30, 30), (1, 6, 90, -150)]),
+    ((2, 8, 16, 24, 2, 64), (3, 7, 7),
+     [(0, 0, 0, 100), (4, 8, 12, 40), (7, 15, 23, 200), (2, 3, 20, 30)]),
+    ((1, 8, 16, 40, 2, 64), (3, 5, 35),
+     [(0, 0, 0, 100), (4, 8, 20, 45), (7, 15, 39, 250)]),
+]
+
+
+def spike_check(shape, ks, spikes, seed, config=None, what="spikes"):
+    from na3d_inputs import make_spike_inputs
+    print("case %s shape=%s window=%s config=%s" % (what, shape, ks, config), flush=True)
+    q, k, v = make_spike_inputs(shape, seed, spikes, "cuda")
+    out = na.fwd(q, k, v, ks, config=config)
+    torch.cuda.synchronize()
+    ref = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), ks)
+    return compare(to_np(out), ref, what)
+
+
+@pytest.mark.parametrize("shape,ks,spikes", SPIKE_CASES, ids=[str(c[:2]) for c in SPIKE_CASES])
+def test_extreme_scores(shape, ks, spikes):
+    spike_check(shape, ks, spikes, 301, what="spikes %s" % (ks,))
+
+
+def spike_variant_cases():
+    """Every rolling instantiation that plans the 11x11x11 (HD 64 and 128) or
+    3x5x27 spike grids."""
+    import ctypes
+    lib = na.load()
+    cases = []
+    for shape, ks, spikes in SPIKE_CASES[:3]:
+        for var in range(na.num_variants()):
+            buf = (ctypes.c_int * 10)()
+            if lib.na3d_plan_config(*shape, *ks, 2, var, 0, buf) == 0:
+                cases.append((var, shape, ks, spikes))
+    return cases
+
+
+@pytest.mark.parametrize("var,shape,ks,spikes", spike_variant_cases(),
+                         ids=lambda x: str(x).replace(" ", "")[:40])
+def test_extreme_scores_each_instantiation(var, shape, ks, spikes):
+    spike_check(shape, ks, spikes, 302 + var, config=(2, var, 0), what="spikes variant %d" % var)
