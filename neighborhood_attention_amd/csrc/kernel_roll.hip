@@ -518,10 +518,37 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   constexpr bool kFixedSwz = RSTEP % 16 == 0;
   const uint32_t d0s = d0 + (kFixedSwz ? (uint32_t)((pc ^ swz(HD, row0)) << 4) : 0u);
   const int full_rounds = total_chunks / NT;  // rounds in which every lane has a chunk
+  // With the swizzle folded in, a lane's offset only advances: by dstep per
+  // round, plus dwrap where its halo column wraps to the next row.  Which
+  // rounds wrap is the same for every plane, so it is worked out once, as a
+  // bit per round (the host keeps every plan within 32 rounds; LDS capacity
+  // alone bounds them by 27).
+  constexpr bool kWrapBits = kFixedSwz;
+  uint32_t wbits = 0;
+  if (kWrapBits) {
+    int rw = rw0;
+    for (int r = 0; r < full_rounds; ++r) {
+      rw += step_w;
+      if (rw >= hwd) {
+        rw -= hwd;
+        wbits |= 1u << r;
+      }
+    }
+  }
   auto issue_stage = [&](int tp, int bufi) {
     const uint16_t* kpl = kbase + (int64_t)tp * a.sk.t;
     const uint16_t* vpl = vbase + (int64_t)tp * a.sv.t;
     const uint32_t dk = lds_addr(smem + bufi * 2 * buf_bytes + wave * kWave * 16);
+    if constexpr (kWrapBits) {
+      uint32_t d = d0s;
+      int r = 0;
+      for (; r < full_rounds; ++r) {
+        dma16_kv(kpl, vpl, d, dk + r * NT * 16, buf_bytes);
+        d += dstep + (dwrap & (uint32_t)__builtin_amdgcn_sbfe((int)wbits, r, 1));
+      }
+      if (r * NT + tid < total_chunks) dma16_kv(kpl, vpl, d, dk + r * NT * 16, buf_bytes);
+      return;
+    }
     uint32_t d = d0s;
     int rw = rw0, row = row0;
     auto advance = [&]() {

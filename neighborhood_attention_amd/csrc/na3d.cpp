@@ -231,6 +231,9 @@ bool plan_roll(int v, const Geom& g, int tile_t, Launch* l, int target = kTarget
   // K and V rows of HD*2 bytes, in one or two plane buffers
   const int64_t lds = 2LL * rv.nbuf * rows * (HD * 2);
   if (lds > kMaxLdsBytes) return false;
+  // the kernel's staging walk keeps one bit per full DMA round of a plane
+  // (at most 32; the LDS limit above already bounds them by 27)
+  if ((int64_t)halo_max * (HD / 8) / (kWave * rv.wh * rv.wt) > 32) return false;
   const int tiles_h = ceil_div(g.box.Hq, BH), tiles_w = ceil_div(g.box.Wq, rv.qw);
   const int64_t spatial = (int64_t)g.B * g.NH * tiles_h * tiles_w;
   const TAxis ax{g.box.Tq, g.box.t0, g.T, g.KT};
