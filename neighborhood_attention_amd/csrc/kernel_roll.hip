@@ -129,12 +129,17 @@ struct Slot {
   float m;            // reference max (natural units), -inf before any key
 };
 
+// Q of one query plane: `base` is the wave-uniform address of the plane in
+// the head, `off` this lane's token offset in bytes (32-bit: the host keeps
+// one head's spatial plane of q and of out below 4 GiB for this family).
 template <int HD>
-__device__ __forceinline__ void load_q(bf16x8 (&qf)[Slot<HD>::KSTEPS], const uint16_t* qp, int g) {
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[Slot<HD>::KSTEPS], const uint16_t* base, uint32_t off,
+                                       int g) {
+  const unsigned char* const qp = reinterpret_cast<const unsigned char*>(base) + off;
 #pragma unroll
   for (int ks = 0; ks < Slot<HD>::KSTEPS; ++ks) {
     const int d = 32 * ks + 8 * g;
-    qf[ks] = d < HD ? *reinterpret_cast<const bf16x8*>(qp + d) : bf16x8{};
+    qf[ks] = d < HD ? *reinterpret_cast<const bf16x8*>(qp + 2 * d) : bf16x8{};
   }
 }
 
@@ -189,14 +194,15 @@ __device__ __forceinline__ void pack_out(const Slot<HD>& S, uint32_t (&pk)[2 * S
 
 // Stores of a packed output (layout of pack_out).
 template <int MT>
-__device__ __forceinline__ void store_out(uint16_t* op, const uint32_t (&pk)[2 * MT], int g) {
+__device__ __forceinline__ void store_out(uint16_t* base, uint32_t off, const uint32_t (&pk)[2 * MT], int g) {
+  unsigned char* const op = reinterpret_cast<unsigned char*>(base) + off;
   if constexpr (MT >= 2) {
 #pragma unroll
     for (int j = 0; j < MT / 2; ++j)
-      *reinterpret_cast<uint4*>(op + 32 * j + 8 * g) =
+      *reinterpret_cast<uint4*>(op + 2 * (32 * j + 8 * g)) =
           make_uint4(pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]);
   } else {
-    *reinterpret_cast<uint2*>(op + 4 * g) = make_uint2(pk[0], pk[1]);
+    *reinterpret_cast<uint2*>(op + 2 * (4 * g)) = make_uint2(pk[0], pk[1]);
   }
 }
 
@@ -491,11 +497,12 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) vofs[mt] = v_addr<HD>(rb + vp, mt, q16);
 
-  // this lane's query token in (b, n) of q and out; plane t adds t * sT
-  const uint16_t* const qbase = a.q + (int64_t)b * a.sq.b + (int64_t)n * a.sq.n +
-                                (int64_t)qhc * a.sq.h + (int64_t)qwc * a.sq.w;
-  uint16_t* const obase = a.o + (int64_t)b * a.so.b + (int64_t)n * a.so.n +
-                          (int64_t)qhc * a.so.h + (int64_t)qwc * a.so.w;
+  // (b, n) of q and out (wave-uniform; plane t adds t * sT), and this
+  // lane's query token within a plane, in bytes
+  const uint16_t* const qbase = a.q + (int64_t)b * a.sq.b + (int64_t)n * a.sq.n;
+  uint16_t* const obase = a.o + (int64_t)b * a.so.b + (int64_t)n * a.so.n;
+  const uint32_t qoff = (uint32_t)(2 * ((int64_t)qhc * a.sq.h + (int64_t)qwc * a.sq.w));
+  const uint32_t ooff = (uint32_t)(2 * ((int64_t)qhc * a.so.h + (int64_t)qwc * a.so.w));
 
   // ---- DMA staging walk: round k moves chunks [k*NT, (k+1)*NT); lane P of a
   // wave lands at chunk P of the buffer (row P / CPR, physical chunk P % CPR).
@@ -628,7 +635,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   bf16x8 qn[KSTEPS];          // Q of query plane qn_t, fetched one key plane early
   int qn_t = -1;
   uint32_t pend[2 * MT];      // packed output of a retired query plane ...
-  uint16_t* pend_p = a.o;     // ... and where it goes
+  uint16_t* pend_p = a.o;     // ... and its plane (wave-uniform)
   bool pend_on = false;
   int t0, t1;
   run_bounds(r_lo, t0, t1);
@@ -662,7 +669,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
 #pragma unroll
               for (int ks = 0; ks < KSTEPS; ++ks) S[s].qf[ks] = qn[ks];
             } else {
-              load_q<HD>(S[s].qf, qbase + (int64_t)tq(jhi) * a.sq.t, g);
+              load_q<HD>(S[s].qf, qbase + (int64_t)tq(jhi) * a.sq.t, qoff, g);
             }
             reset_state(S[s]);
           }
@@ -673,7 +680,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       if (pend_on) {
-        if (qvalid) store_out<MT>(pend_p, pend, g);
+        if (qvalid) store_out<MT>(pend_p, ooff, pend, g);
         pend_on = false;
       }
       const int nxt = tp + 1 < p1 ? tp + 1 : np0;  // plane of the next step, -1 = none
@@ -710,7 +717,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
           tn = nt0 + it;
         }
         if (tn >= 0) {
-          load_q<HD>(qn, qbase + (int64_t)tn * a.sq.t, g);
+          load_q<HD>(qn, qbase + (int64_t)tn * a.sq.t, qoff, g);
           qn_t = tn;
         }
       }
@@ -894,7 +901,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
       while (jlo <= jhi && wst(tq(jlo)) + KT - 1 == tp) {
         const int sl = jlo % NS;
         if (active) {
-          if (pend_on && qvalid) store_out<MT>(pend_p, pend, g);
+          if (pend_on && qvalid) store_out<MT>(pend_p, ooff, pend, g);
 #pragma unroll
           for (int s = 0; s < NS; ++s)
             if (s == sl) pack_out<HD>(S[s], pend);
@@ -910,7 +917,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
       }
     }
   }
-  if (pend_on && qvalid) store_out<MT>(pend_p, pend, g);
+  if (pend_on && qvalid) store_out<MT>(pend_p, ooff, pend, g);
 }
 
 template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>

@@ -79,14 +79,16 @@ int64_t extent(const Strides& s, int B, int T, int H, int W, int NH, int HD) {
   return e < ((int64_t)1 << 62) ? e : -1;
 }
 
-// Bytes spanned by the spatial (H, W) part of one K/V plane of one head: the
-// rolling family stages it with 32-bit byte offsets.
+// Bytes spanned by the spatial (H, W) part of one plane of one head of a
+// tensor: the rolling family addresses K/V staging, Q loads and output
+// stores within such a plane with 32-bit byte offsets.
 int64_t kv_span_bytes(const Strides& sk, int H, int W, int HD) {
   return 2 * ((int64_t)(H - 1) * sk.h + (int64_t)(W - 1) * sk.w + HD);
 }
 
 // Everything a plan depends on: the k/v grid, heads, head dim, window, the
-// query box, and the bytes spanned by one head's spatial K/V plane.
+// query box, and the most bytes one head's spatial plane of k, v, q or out
+// spans.
 struct Geom {
   int B, T, H, W, NH, HD, KT, KH, KW;
   Box box;
@@ -218,7 +220,8 @@ bool plan_roll(int v, const Geom& g, int tile_t, Launch* l, int target = kTarget
   const RollVariant& rv = kRollVariants[v];
   const int HD = g.HD, KH = g.KH, KW = g.KW, H = g.H, W = g.W;
   if (rv.hd != HD) return false;
-  // staging offsets are 32-bit byte offsets within one head's K/V plane
+  // staging, Q and output offsets are 32-bit byte offsets within one head's
+  // spatial plane
   if (g.kv_span >= ((int64_t)1 << 32)) return false;
   const int BH = rv.wh * rv.qh;
   const int hwd_max = std::min(rv.qw + KW - 1, W);
@@ -509,7 +512,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, Geom g, con
              int family, int variant, int tile_t, void* stream) {
   int rc = check_all(q, k, v, out, g, st);
   if (rc != NA3D_OK) return rc;
-  g.kv_span = kv_span_bytes(st[1], g.H, g.W, g.HD);
+  g.kv_span = std::max({kv_span_bytes(st[1], g.H, g.W, g.HD), kv_span_bytes(st[2], g.H, g.W, g.HD),
+                        kv_span_bytes(st[0], g.box.Hq, g.box.Wq, g.HD),
+                        kv_span_bytes(st[3], g.box.Hq, g.box.Wq, g.HD)});
   Launch l;
   rc = cached_plan(g, family, variant, tile_t, &l);
   if (rc != NA3D_OK) return rc;
