@@ -109,8 +109,8 @@ struct Launch {
 };
 
 // Instantiations of the rolling family: index, head dim, query block
-// (QH x QW = 16 queries per wave), wave grid (WH block rows x WT query-plane
-// phases), query-plane slots per wave, 16-key tiles per softmax group, most
+// (QH x QW queries of 16 / (QH x QW) consecutive query planes: 16 queries per
+// wave), wave grid (WH block rows x WT query-plane phases), query-plane slots per wave, 16-key tiles per softmax group, most
 // groups a wave's window union may need, staged plane buffers (1 or 2), and
 // the waves per SIMD the register allocation must leave room for (0 = the
 // compiler's choice; 4 caps it at 128 VGPRs).
@@ -173,7 +173,10 @@ struct Launch {
   X(55, 64, 2, 8, 2, 4, 1, 7, 3, 1, 0) \
   X(56, 64, 2, 8, 2, 4, 1, 7, 4, 1, 0) \
   X(57, 128, 2, 8, 1, 4, 1, 9, 2, 1, 0) \
-  X(58, 64, 2, 8, 1, 4, 1, 9, 2, 1, 0)
+  X(58, 64, 2, 8, 1, 4, 1, 9, 2, 1, 0) \
+  X(59, 64, 2, 4, 2, 2, 1, 11, 1, 1, 0) \
+  X(60, 64, 2, 4, 4, 1, 1, 11, 1, 1, 0) \
+  X(61, 128, 2, 4, 2, 2, 1, 11, 1, 1, 0)
 
 struct RollVariant {
   int hd, qh, qw, wh, wt, ns, nk, ng, nbuf, occ;

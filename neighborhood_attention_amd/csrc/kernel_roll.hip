@@ -281,7 +281,12 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
 // one tile of a batch).
 template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
 __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
-  static_assert(QH * QW == 16, "a wave owns 16 queries");
+  // A wave owns 16 queries: a QH x QW block of PT consecutive query planes
+  // (PT = 2 for 8-query spatial blocks: the union of their windows is
+  // smaller per plane, and a key plane is shared by both planes' queries).
+  constexpr int BQ = QH * QW;  // queries of one plane in a block
+  constexpr int PT = 16 / BQ;
+  static_assert(BQ * PT == 16 && (PT == 1 || PT == 2), "a wave owns 16 queries");
   static_assert(NBUF == 1 || NBUF == 2, "one or two plane buffers");
   constexpr int KSTEPS = Slot<HD>::KSTEPS;
   constexpr int MT = Slot<HD>::MT;
@@ -296,6 +301,9 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   // window masks as an fp32 accumulator-input table (see below) when a wave
   // reads at most 7 tiles per key plane, else as bf16 pairs applied by MFMA
   constexpr bool kMaskTable = NG * NK <= 7;
+  // two-plane blocks take their per-plane window (along T) as the start
+  // value of the mask MFMA, with one slot per wave
+  static_assert(PT == 1 || (!kMaskTable && NS == 1), "two-plane blocks: mask MFMA, one slot");
   // V^T operands of all ones (bf16 1.0): the MFMA against P^T sums the
   // weights of each query, already reduced over its four lanes
   const bf16x8 kOnes8 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
@@ -372,9 +380,11 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   // ---- this wave's block of 16 queries
   const int bh0 = h0 + ih * QH;
   const bool active = bh0 < Hq;
-  const int qh = bh0 + q16 / QW;
-  const int qw = w0 + q16 % QW;
-  const bool qvalid = active && qh < Hq && qw < Wq;
+  const int pt = q16 / BQ;  // this lane's plane within the block (PT > 1)
+  const int qr = q16 % BQ;  // and its query within that plane's block
+  const int qh = bh0 + qr / QW;
+  const int qw = w0 + qr % QW;
+  const bool qvalid = active && qh < Hq && qw < Wq;  // spatially
   const int qhc = min(qh, Hq - 1), qwc = min(qw, Wq - 1);
   // union of the block's windows = staged rows [base, base + un); the wave
   // reads rows [rb, rb + NG * GK), which hold the union (the host checks
@@ -391,7 +401,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   int ah[4], aw[4];  // window starts of queries 4g + j, relative to the halo
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int qi = 4 * g + j;
+    const int qi = (4 * g + j) % BQ;
     const int qhj = bh0 + qi / QW, qwj = w0 + qi % QW;
     const bool ok = active && qhj < Hq && qwj < Wq;
     ah[j] = ok ? wsh(qhj) - hh0 : -(1 << 20);
@@ -445,7 +455,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   // the variant intact.
   f32x4 mc[kMaskTable ? NG : 1][kMaskTable ? NK : 1];
   if constexpr (kMaskTable) {
-    const int qhm = bh0 + q16 / QW, qwm = w0 + q16 % QW;
+    const int qhm = bh0 + qr / QW, qwm = w0 + qr % QW;
     const bool okm = active && qhm < Hq && qwm < Wq;
     // window start of this lane's query, relative to the halo
     const int ahm = okm ? wsh(qhm) - hh0 : -(1 << 20);
@@ -503,6 +513,12 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   uint16_t* const obase = a.o + (int64_t)b * a.so.b + (int64_t)n * a.so.n;
   const uint32_t qoff = (uint32_t)(2 * ((int64_t)qhc * a.sq.h + (int64_t)qwc * a.sq.w));
   const uint32_t ooff = (uint32_t)(2 * ((int64_t)qhc * a.so.h + (int64_t)qwc * a.so.w));
+  // with two-plane blocks, the same for the lane's plane pt of a block
+  // (32-bit: the host keeps one plane step plus one spatial plane below
+  // 4 GiB for these variants); qoff alone where that plane is past the box
+  const uint32_t qoff_pt = qoff + (uint32_t)pt * (uint32_t)(2 * a.sq.t);
+  const uint32_t ooff_pt = ooff + (uint32_t)pt * (uint32_t)(2 * a.so.t);
+  auto q_lane = [&](int t) { return (PT > 1 && t + PT - 1 >= a.Tq) ? qoff : qoff_pt; };
 
   // ---- DMA staging walk: round k moves chunks [k*NT, (k+1)*NT); lane P of a
   // wave lands at chunk P of the buffer (row P / CPR, physical chunk P % CPR).
@@ -582,7 +598,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   // flight at a key plane stage the next one while the others compute (the
   // compute of a key plane is long enough to cover the slower issue; at
   // smaller HD the plane then lands late and this measured slower).
-  constexpr bool kIdleStaging = NBUF == 2 && HD >= 128;
+  constexpr bool kIdleStaging = NBUF == 2 && HD >= 128 && PT == 1;
   auto issue_stage_by = [&](int tp, int bufi, int rank, int nst) {
     const uint16_t* kpl = kbase + (int64_t)tp * a.sk.t;
     const uint16_t* vpl = vbase + (int64_t)tp * a.sv.t;
@@ -637,6 +653,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   uint32_t pend[2 * MT];      // packed output of a retired query plane ...
   uint16_t* pend_p = a.o;     // ... and its plane (wave-uniform)
   bool pend_on = false;
+  bool pend_ok = false;       // ... and whether this lane's query is stored
   int t0, t1;
   run_bounds(r_lo, t0, t1);
   issue_stage(wst(t0), 0);  // step st uses buffer st % NBUF
@@ -649,8 +666,10 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
       run_bounds(ri + 1, nt0, nt1);
       np0 = wst(nt0);
     }
-    auto tq = [&](int j) { return t0 + it + WT * j; };
-    int jlo = 0, jhi = -1;  // query planes j in [jlo, jhi] are in flight
+    // this wave's blocks: block j covers query planes [tq(j), tq_last(j)]
+    auto tq = [&](int j) { return t0 + PT * (it + WT * j); };
+    auto tq_last = [&](int j) { return min(tq(j) + PT - 1, t1 - 1); };
+    int jlo = 0, jhi = -1;  // blocks j in [jlo, jhi] are in flight
     // query planes [alo, ahi] of the run (any wave) are in flight
     int alo = t0, ahi = t0 - 1;
     for (int tp = p0; tp < p1; ++tp, ++st) {
@@ -669,7 +688,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
 #pragma unroll
               for (int ks = 0; ks < KSTEPS; ++ks) S[s].qf[ks] = qn[ks];
             } else {
-              load_q<HD>(S[s].qf, qbase + (int64_t)tq(jhi) * a.sq.t, qoff, g);
+              load_q<HD>(S[s].qf, qbase + (int64_t)tq(jhi) * a.sq.t, q_lane(tq(jhi)), g);
             }
             reset_state(S[s]);
           }
@@ -680,7 +699,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       if (pend_on) {
-        if (qvalid) store_out<MT>(pend_p, ooff, pend, g);
+        if (pend_ok) store_out<MT>(pend_p, ooff_pt, pend, g);
         pend_on = false;
       }
       const int nxt = tp + 1 < p1 ? tp + 1 : np0;  // plane of the next step, -1 = none
@@ -713,16 +732,26 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
         int tn = -1;
         if (tp + 1 < p1) {
           if (tq(jhi + 1) < t1 && wst(tq(jhi + 1)) == tp + 1) tn = tq(jhi + 1);
-        } else if (np0 >= 0 && nt0 + it < nt1 && wst(nt0 + it) == np0) {
-          tn = nt0 + it;
+        } else if (np0 >= 0 && nt0 + PT * it < nt1 && wst(nt0 + PT * it) == np0) {
+          tn = nt0 + PT * it;
         }
         if (tn >= 0) {
-          load_q<HD>(qn, qbase + (int64_t)tn * a.sq.t, qoff, g);
+          load_q<HD>(qn, qbase + (int64_t)tn * a.sq.t, q_lane(tn), g);
           qn_t = tn;
         }
       }
 
       if (active && jhi >= jlo) {
+        // two-plane blocks: key plane tp is outside the window of a lane
+        // whose query plane does not reach it (or lies past the run); its
+        // scores then start at -2^100 on top of the spatial mask
+        f32x4 tb4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (PT > 1) {
+          const int tl = tq(jlo) + pt;
+          const bool in = tl < t1 && wst(tl) <= tp && tp < wst(tl) + KT;
+          const float tb = in ? 0.f : __builtin_bit_cast(float, kMaskBits << 16);
+          tb4 = f32x4{tb, tb, tb, tb};
+        }
         const unsigned char* lk = smem + (NBUF == 2 ? (st & 1) : 0) * 2 * buf_bytes;
         const unsigned char* lv = lk + buf_bytes;
         // Work unit u = (group u / NS, slot u % NS).  Units run as a software
@@ -760,8 +789,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
                 out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], S[sl].qf[0], mc[gi][c], 0, 0, 0);
               } else {
                 out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, mk[gi][c >> 1]), (c & 1) ? ident_o : ident_e,
-                    f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, mk[gi][c >> 1]), (c & 1) ? ident_o : ident_e, tb4, 0, 0, 0);
                 out[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], S[sl].qf[0], out[c], 0, 0, 0);
               }
 #pragma unroll
@@ -784,7 +812,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
                   if (c0 + t < NK)
                     out[c0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8, mk[gi][(c0 + t) >> 1]),
-                        ((c0 + t) & 1) ? ident_o : ident_e, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        ((c0 + t) & 1) ? ident_o : ident_e, tb4, 0, 0, 0);
               }
 #pragma unroll
               for (int ks = 0; ks < KSTEPS; ++ks)
@@ -898,14 +926,15 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
       // retire this wave's query planes whose window ends here; the output
       // waits in registers for the next barrier (a second one in the same
       // plane is stored at once)
-      while (jlo <= jhi && wst(tq(jlo)) + KT - 1 == tp) {
+      while (jlo <= jhi && wst(tq_last(jlo)) + KT - 1 == tp) {
         const int sl = jlo % NS;
         if (active) {
-          if (pend_on && qvalid) store_out<MT>(pend_p, ooff, pend, g);
+          if (pend_on && pend_ok) store_out<MT>(pend_p, ooff_pt, pend, g);
 #pragma unroll
           for (int s = 0; s < NS; ++s)
             if (s == sl) pack_out<HD>(S[s], pend);
           pend_p = obase + (int64_t)tq(jlo) * a.so.t;
+          pend_ok = qvalid && tq(jlo) + pt < t1;
           pend_on = true;
         }
         ++jlo;
@@ -917,7 +946,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
       }
     }
   }
-  if (pend_on && qvalid) store_out<MT>(pend_p, ooff, pend, g);
+  if (pend_on && pend_ok) store_out<MT>(pend_p, ooff_pt, pend, g);
 }
 
 template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
