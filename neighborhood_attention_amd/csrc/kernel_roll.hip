@@ -8,10 +8,15 @@
 // Workgroup (WG) = batch b, head n, a (WH*QH) x QW spatial tile and a run of
 // consecutive query planes [t0, t1).  The WG is a WH x WT grid of waves: wave
 // (ih, it) owns the QH x QW block of 16 queries in block row ih, for the query
-// planes t0 + it, t0 + it + WT, ... of the run.  All waves share the same
-// query columns, so the union of a block's windows is one contiguous range of
-// the staged halo rows, and every K/V operand address is a lane constant plus
-// a compile-time tile offset.
+// planes t0 + it, t0 + it + WT, ... of the run.  With QH x QW = 8 a block
+// holds QH x QW queries on each of two consecutive planes (wave it owns the
+// plane pairs starting at t0 + 2 it, t0 + 2 (it + WT), ...); both planes read
+// the same key planes except the first and the last of the pair's windows,
+// where the other plane's queries are masked, and the smaller spatial block
+// has a smaller window union per plane.  All waves share the same query
+// columns, so the union of a block's windows is one contiguous range of the
+// staged halo rows, and every K/V operand address is a lane constant plus a
+// compile-time tile offset.
 //
 // The WG streams the key planes of its runs in order.  Each plane's K/V halo
 // is staged in LDS once, with direct global->LDS loads (global_load_lds
