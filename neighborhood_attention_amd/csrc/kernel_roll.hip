@@ -306,9 +306,9 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   // window masks as an fp32 accumulator-input table (see below) when a wave
   // reads at most 7 tiles per key plane, else as bf16 pairs applied by MFMA
   constexpr bool kMaskTable = NG * NK <= 7;
-  // two-plane blocks take their per-plane window (along T) as the start
-  // value of the mask MFMA, with one slot per wave
-  static_assert(PT == 1 || (!kMaskTable && NS == 1), "two-plane blocks: mask MFMA, one slot");
+  // two-plane blocks apply their per-plane window along T per key plane (see
+  // the compute step), with one slot per wave
+  static_assert(PT == 1 || NS == 1, "two-plane blocks: one slot");
   // V^T operands of all ones (bf16 1.0): the MFMA against P^T sums the
   // weights of each query, already reduced over its four lanes
   const bf16x8 kOnes8 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
@@ -523,7 +523,11 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   // 4 GiB for these variants); qoff alone where that plane is past the box
   const uint32_t qoff_pt = qoff + (uint32_t)pt * (uint32_t)(2 * a.sq.t);
   const uint32_t ooff_pt = ooff + (uint32_t)pt * (uint32_t)(2 * a.so.t);
-  auto q_lane = [&](int t) { return (PT > 1 && t + PT - 1 >= a.Tq) ? qoff : qoff_pt; };
+  // Q of the block at plane t (lanes whose plane is past the box keep stale
+  // registers: their queries are masked and never stored)
+  auto load_q_block = [&](bf16x8 (&qf)[KSTEPS], int t) __attribute__((always_inline)) {
+    if (PT == 1 || t + pt < a.Tq) load_q<HD>(qf, qbase + (int64_t)t * a.sq.t, qoff_pt, g);
+  };
 
   // ---- DMA staging walk: round k moves chunks [k*NT, (k+1)*NT); lane P of a
   // wave lands at chunk P of the buffer (row P / CPR, physical chunk P % CPR).
@@ -693,7 +697,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
 #pragma unroll
               for (int ks = 0; ks < KSTEPS; ++ks) S[s].qf[ks] = qn[ks];
             } else {
-              load_q<HD>(S[s].qf, qbase + (int64_t)tq(jhi) * a.sq.t, q_lane(tq(jhi)), g);
+              load_q_block(S[s].qf, tq(jhi));
             }
             reset_state(S[s]);
           }
@@ -741,20 +745,23 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
           tn = nt0 + PT * it;
         }
         if (tn >= 0) {
-          load_q<HD>(qn, qbase + (int64_t)tn * a.sq.t, q_lane(tn), g);
+          load_q_block(qn, tn);
           qn_t = tn;
         }
       }
 
       if (active && jhi >= jlo) {
         // two-plane blocks: key plane tp is outside the window of a lane
-        // whose query plane does not reach it (or lies past the run); its
-        // scores then start at -2^100 on top of the spatial mask
+        // whose query plane does not reach it (or lies past the run).  With
+        // the mask MFMA its scores then start at -2^100 on top of the spatial
+        // mask; with the mask table its max is left out (the reference max
+        // stays) and its weights are computed against +2^100, i.e. are 0
         f32x4 tb4 = {0.f, 0.f, 0.f, 0.f};
+        bool tout = false;
         if constexpr (PT > 1) {
           const int tl = tq(jlo) + pt;
-          const bool in = tl < t1 && wst(tl) <= tp && tp < wst(tl) + KT;
-          const float tb = in ? 0.f : __builtin_bit_cast(float, kMaskBits << 16);
+          tout = !(tl < t1 && wst(tl) <= tp && tp < wst(tl) + KT);
+          const float tb = tout ? __builtin_bit_cast(float, kMaskBits << 16) : 0.f;
           tb4 = f32x4{tb, tb, tb, tb};
         }
         const unsigned char* lk = smem + (NBUF == 2 ? (st & 1) : 0) * 2 * buf_bytes;
@@ -784,7 +791,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
           // dependent MFMA never waits directly on the previous one; one tile
           // at a time where a second K fragment set would not fit the register
           // cap of the variant.
-          constexpr int kPair = (OCC > 0 && NG > 1) ? 1 : 2;
+          constexpr int kPair = (OCC > 0 && (NG > 1 || PT > 1)) ? 1 : 2;
           if constexpr (kPair == 1) {
 #pragma unroll
             for (int c = 0; c < NK; ++c) {
@@ -847,6 +854,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
             mx = __builtin_fmaxf(__builtin_fmaxf(mx, in[i >> 2][i & 3]), in[(i + 1) >> 2][(i + 1) & 3]);
           if ((4 * NK - 3) & 1) mx = __builtin_fmaxf(mx, in[NK - 1][3]);
           mx = xmax4(mx);
+          if constexpr (PT > 1 && kMaskTable) mx = tout ? kNegInf : mx;
           if (__builtin_amdgcn_ballot_w64(mx > S[sl].m + kRescale && mx > kRealScore) != 0) {
             const float mn = mx > kRealScore ? fmaxf(S[sl].m, mx) : S[sl].m;
             const float alpha = S[sl].m == kNegInf ? 0.f : __builtin_amdgcn_exp2f((S[sl].m - mn) * kLog2e);
@@ -860,7 +868,8 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
         // with zero weights)
         auto unit_exp = [&](int u, const f32x4 (&in)[NK], bf16x8 (&out)[NPP]) __attribute__((always_inline)) {
           const int sl = u % NS;
-          const float mb = S[sl].m == kNegInf ? 0.f : S[sl].m * kLog2e;
+          float mb = S[sl].m == kNegInf ? 0.f : S[sl].m * kLog2e;
+          if constexpr (PT > 1 && kMaskTable) mb = tout ? 0x1p100f : mb;
 #pragma unroll
           for (int c = 0; c < NK; ++c) {
 #pragma unroll

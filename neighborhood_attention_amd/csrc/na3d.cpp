@@ -338,6 +338,13 @@ int pick_roll(const Geom& g, Launch* l) {
     case 128: pref = p128; np = (int)(sizeof(p128) / sizeof(int)); break;
     default: pref = p256; np = (int)(sizeof(p256) / sizeof(int)); break;
   }
+  // head dim 128, three-plane windows: blocks of 2x4 queries on two planes,
+  // 8 waves as 4 block rows by 2 plane-pair phases (a wave's consecutive
+  // pairs are four planes apart, so their windows never overlap and every
+  // wave works on every key plane, where 2x8 blocks on single planes leave
+  // one phase in four idle): 4653 against 4952 us on the 32x128x192,
+  // 16-head grid
+  if (g.HD == 128 && g.KT == 3 && plan_roll(62, g, 0, l)) return 1;
   for (int i = 0; i < np; ++i) {
     if (!plan_roll(pref[i], g, 0, l)) continue;
     // windows much wider than tall, on a grid large enough that the 8-wave
@@ -357,13 +364,14 @@ int pick_roll(const Geom& g, Launch* l) {
       Launch alt;
       if (plan_roll(34, g, 0, &alt)) *l = alt;
     }
-    // query blocks over two planes (2x4 queries on each): where their
-    // smaller window union saves more tiles than the extra key plane per
-    // block costs, i.e. (KT + 1) x 11 tiles per 16 queries against KT x the
-    // chosen variant's, by at least 5% (11x11x11: 3% faster at head dim 64
-    // on 16x48x64, 6% on 16x80x32 at 32 heads, 7% at head dim 128)
+    // query blocks over two planes (2x4 queries on each), for windows long
+    // along T: where their smaller window union saves more tiles than the
+    // extra key plane per block costs, i.e. (KT + 1) x 11 tiles per 16
+    // queries against KT x the chosen variant's, by at least 5% (11x11x11:
+    // 3% faster at head dim 64 on 16x48x64, 6% on 16x80x32 at 32 heads, 7%
+    // at head dim 128)
     const int pp = g.HD == 64 ? 59 : (g.HD == 128 ? 61 : -1);
-    if (pp >= 0) {
+    if (pp >= 0 && g.KT >= 6) {
       const RollVariant& a = kRollVariants[l->variant];
       const RollVariant& c = kRollVariants[pp];
       const int64_t ca = (int64_t)(g.KT + 16 / (a.qh * a.qw) - 1) * a.ng * a.nk;
