@@ -922,15 +922,15 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
           } else {
             pin(pf[u & 1]);
             // one query plane: its products must land before the next
-            // unit's max may rescale the running output.  With 13-tile
-            // groups the P.V phase runs at a raised wave priority, so a wave
-            // entering it issues its MFMAs ahead of the co-resident waves'
-            // softmax work and the MFMA and VALU phases of the waves on a
-            // SIMD stay staggered (3% on the 11x11x11 grid; no change on the
-            // 7-tile variants, where it is left out)
-            if constexpr (NK >= 13) __builtin_amdgcn_s_setprio(2);
+            // unit's max may rescale the running output.  With 11- and
+            // 13-tile groups the P.V phase runs at a raised wave priority, so
+            // a wave entering it issues its MFMAs ahead of the co-resident
+            // waves' softmax work and the MFMA and VALU phases of the waves on
+            // a SIMD stay staggered (3-4% on the 11x11x11 grid; no change on
+            // the 7-tile variants, where it is left out)
+            if constexpr (NK >= 11) __builtin_amdgcn_s_setprio(2);
             unit_pv(u, pf[u & 1]);
-            if constexpr (NK >= 13) __builtin_amdgcn_s_setprio(0);
+            if constexpr (NK >= 11) __builtin_amdgcn_s_setprio(0);
             if (u + 1 < NU) unit_max(u + 1, sc[(u + 1) & 1]);
           }
         }
