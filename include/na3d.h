@@ -305,6 +305,21 @@ int na3d_rms_norm_config(const void* x, const void* weight, void* y, int rows,
 /* Number of rolling-family instantiations compiled into the library. */
 int na3d_num_variants(void);
 
+/*
+ * The compile-time shape of rolling instantiation `variant` (for tuning and
+ * tests that pick configurations through na3d_fwd_config):
+ *   info: host array of 10 ints, written on success: [0] head dim, [1] QH
+ *         and [2] QW, the query block on one plane (16 / (QH*QW) consecutive
+ *         query planes per block, 1 or 2), [3] WH block rows and [4] WT
+ *         query-plane phases per workgroup (WH*WT waves of 64 lanes), [5]
+ *         query-plane slots per wave, [6] 16-key tiles per softmax group, [7]
+ *         groups, [8] staged plane buffers (1 or 2), [9] waves per SIMD the
+ *         register allocation is capped for (0 = no cap).
+ * Returns NA3D_OK, NA3D_ERR_NULL (info is NULL) or NA3D_ERR_CONFIG (variant
+ * outside 0 .. na3d_num_variants()-1).  No device calls.
+ */
+int na3d_variant_info(int variant, int* info);
+
 /* Library ABI version (incremented on incompatible changes). */
 int na3d_abi_version(void);
 

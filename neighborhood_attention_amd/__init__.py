@@ -39,7 +39,7 @@ EXPORTS = ("na3d_fwd", "na3d_check_args", "na3d_status_string", "na3d_plan",
            "na3d_fwd_strided_config", "na3d_fwd_subgrid", "na3d_check_args_subgrid",
            "na3d_fwd_subgrid_config", "na3d_rms_norm", "na3d_check_args_rms_norm",
            "na3d_rms_norm_config", "na3d_fwd_batch", "na3d_check_args_batch",
-           "na3d_plan_batch", "na3d_num_variants", "na3d_abi_version")
+           "na3d_plan_batch", "na3d_num_variants", "na3d_variant_info", "na3d_abi_version")
 PLAN_KEYS = ("family", "tile_t", "tile_h", "tile_w", "workgroups", "threads", "lds_bytes",
              "planes", "variant", "runs")
 
@@ -113,6 +113,8 @@ def load(path: str = LIB_PATH):
         lib.na3d_plan_batch.restype = i32
         lib.na3d_num_variants.argtypes = []
         lib.na3d_num_variants.restype = i32
+        lib.na3d_variant_info.argtypes = [i32, ctypes.POINTER(i32)]
+        lib.na3d_variant_info.restype = i32
         lib.na3d_abi_version.argtypes = []
         lib.na3d_abi_version.restype = i32
         _lib = lib
@@ -185,6 +187,20 @@ def plan(shape, kernel_size, family: int = 0, variant: int = 0, tile_t: int = 0)
 
 def num_variants() -> int:
     return int(load().na3d_num_variants())
+
+
+VARIANT_FIELDS = ("hd", "qh", "qw", "wh", "wt", "ns", "nk", "ng", "nbuf", "occ")
+
+
+def variant_info(variant: int) -> dict:
+    """Compile-time shape of a rolling instantiation (na3d_variant_info):
+    head dim, query block QH x QW on each of 16 / (QH*QW) planes, wave grid,
+    slots, tiles per group, groups, plane buffers, occupancy cap."""
+    buf = (ctypes.c_int * 10)()
+    rc = load().na3d_variant_info(int(variant), buf)
+    if rc != NA3D_OK:
+        raise NA3DError(rc, "na3d_variant_info")
+    return dict(zip(VARIANT_FIELDS, (int(x) for x in buf)))
 
 
 def fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, shape, kernel_size,

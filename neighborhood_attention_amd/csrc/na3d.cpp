@@ -344,7 +344,7 @@ int pick_roll(const Geom& g, Launch* l) {
   // wave works on every key plane, where 2x8 blocks on single planes leave
   // one phase in four idle): 4653 against 4952 us on the 32x128x192,
   // 16-head grid
-  if (g.HD == 128 && g.KT == 3 && plan_roll(62, g, 0, l)) return 1;
+  if (g.HD == 128 && g.KT == 3 && plan_roll(61, g, 0, l)) return 1;
   for (int i = 0; i < np; ++i) {
     if (!plan_roll(pref[i], g, 0, l)) continue;
     // windows much wider than tall, on a grid large enough that the 8-wave
@@ -370,7 +370,7 @@ int pick_roll(const Geom& g, Launch* l) {
     // queries against KT x the chosen variant's, by at least 5% (11x11x11:
     // 3% faster at head dim 64 on 16x48x64, 6% on 16x80x32 at 32 heads, 7%
     // at head dim 128)
-    const int pp = g.HD == 64 ? 59 : (g.HD == 128 ? 61 : -1);
+    const int pp = g.HD == 64 ? 59 : (g.HD == 128 ? 60 : -1);
     if (pp >= 0 && g.KT >= 6) {
       const RollVariant& a = kRollVariants[l->variant];
       const RollVariant& c = kRollVariants[pp];
@@ -771,6 +771,15 @@ extern "C" {
 int na3d_abi_version(void) { return 3; }
 
 int na3d_num_variants(void) { return kNumRollVariants; }
+
+int na3d_variant_info(int variant, int* info) {
+  if (!info) return NA3D_ERR_NULL;
+  if (variant < 0 || variant >= kNumRollVariants) return NA3D_ERR_CONFIG;
+  const RollVariant& v = kRollVariants[variant];
+  const int vals[10] = {v.hd, v.qh, v.qw, v.wh, v.wt, v.ns, v.nk, v.ng, v.nbuf, v.occ};
+  for (int i = 0; i < 10; ++i) info[i] = vals[i];
+  return NA3D_OK;
+}
 
 const char* na3d_status_string(int status) {
   switch (status) {

@@ -42,6 +42,22 @@ def test_abi_version():
     assert na.load().na3d_abi_version() == 3
 
 
+def test_variant_info():
+    n = na.num_variants()
+    assert n > 0
+    for v in range(n):
+        info = na.variant_info(v)
+        assert info["hd"] in (16, 32, 64, 128, 256)
+        assert info["qh"] * info["qw"] in (8, 16)          # 16 queries over 2 or 1 planes
+        assert info["wh"] * info["wt"] * 64 <= 1024
+        assert info["nbuf"] in (1, 2) and info["ns"] >= 1 and info["nk"] >= 1 and info["ng"] >= 1
+    lib = na.load()
+    buf = (ctypes.c_int * 10)()
+    assert lib.na3d_variant_info(-1, buf) == na.NA3D_ERR_CONFIG
+    assert lib.na3d_variant_info(n, buf) == na.NA3D_ERR_CONFIG
+    assert lib.na3d_variant_info(0, None) == na.NA3D_ERR_NULL
+
+
 def check(ptrs=(A, B_, C, O), shape=SHAPE, ks=KS):
     return na.check_args(*ptrs, shape, ks)
 

@@ -308,6 +308,38 @@ def test_each_instantiation(fam, var, shape, ks):
     compare(to_np(out), ref, "family %d variant %d" % (fam, var))
 
 
+def two_plane_cases():
+    """Instantiations whose blocks hold 2x4 queries on each of two query
+    planes, on grids with one, three, five, seven or thirteen planes (a
+    block's second plane then lies past the grid or its run, and the first
+    and last key planes of a pair are in window for one plane only), with
+    ragged spatial tiles."""
+    import ctypes
+    lib = na.load()
+    cases = []
+    for var in range(na.num_variants()):
+        info = na.variant_info(var)
+        if info["qh"] * info["qw"] != 8:
+            continue
+        for shape, ks in [((1, 1, 9, 13, 2), (1, 9, 11)), ((1, 3, 9, 13, 1), (3, 7, 7)),
+                          ((1, 5, 13, 14, 1), (5, 9, 9)), ((1, 7, 12, 16, 1), (7, 11, 11)),
+                          ((2, 2, 6, 7, 1), (1, 5, 5)), ((1, 13, 14, 15, 1), (11, 11, 11))]:
+            sh = shape + (info["hd"],)
+            buf = (ctypes.c_int * 10)()
+            if lib.na3d_plan_config(*sh, *ks, 2, var, 0, buf) == 0:
+                cases.append((var, sh, ks))
+    return cases
+
+
+@pytest.mark.parametrize("var,shape,ks", two_plane_cases(), ids=lambda x: str(x).replace(" ", ""))
+def test_two_plane_blocks(var, shape, ks):
+    print("case two-plane variant=%d shape=%s window=%s" % (var, shape, ks), flush=True)
+    q, k, v = inputs_on_gpu(shape, 1000 + var)
+    out = na.fwd(q, k, v, ks, config=(2, var, 0))
+    torch.cuda.synchronize()
+    compare(to_np(out), oracle.fwd(q.cpu(), k.cpu(), v.cpu(), ks), "two-plane variant %d" % var)
+
+
 @pytest.mark.parametrize("tile_t", [1, 2, 3, 5, 16])
 def test_rolling_run_lengths(tile_t):
     """Query-plane runs of any length give the same result (admission and
