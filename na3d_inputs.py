@@ -82,8 +82,11 @@ WORKLOADS = {
                  note="anisotropic wide window; grid of the aiter PR's (3,5,27) "
                       "benchmark row (its head count is not stated; 8 here)"),
         Workload("window_19", (1, 24, 32, 32, 4, 64), (19, 19, 19), 8,
-                 note="a window whose union exceeds every rolling instantiation: the "
-                      "general family's case"),
+                 note="a 484-key window union per 4x4 query block: the four-group "
+                      "rolling instantiation"),
+        Workload("window_19_hd128", (1, 24, 32, 32, 2, 128), (19, 19, 19), 9,
+                 note="the same window at head dim 128, whose halo no rolling "
+                      "instantiation's LDS holds: the general family's case"),
         Workload("wide_w41", (1, 4, 8, 128, 8, 64), (3, 5, 41), 7,
                  note="a window wider than 33 along W (the Triton kernel's shape gate "
                       "sent these to tiled SDPA) on the same grid"),

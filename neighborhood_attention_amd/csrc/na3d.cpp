@@ -310,7 +310,11 @@ int pick_roll(const Geom& g, Launch* l) {
   // windows wider than 33 that the pages' kernel refused: measured 1.9-2.8x
   // faster than the 4x4 two-group variant 10 and 3.5x faster than the
   // general family on (3,5,35) to (3,5,63))
-  static const int p64_large[] = {5, 46, 51, 50, 49, 58, 55, 56, 10, 22, 6, 7, 9};
+  // and, last, four 8-tile groups (512 keys) on 4x4 blocks for unions no
+  // smaller instantiation holds, one 8-wave workgroup per CU (19x19x19 on
+  // 24x32x32, 4 heads: 384 us against 1687 us for the general family;
+  // (5,19,19) on 8x32x64: 88 against 317 us)
+  static const int p64_large[] = {5, 46, 51, 50, 49, 58, 55, 56, 10, 22, 6, 7, 9, 62};
   // head dim 128: 4x4 blocks (one 13-tile group) before the 2x8 two-group
   // variants for near-cubic windows (11x11x11 on 16x48x64, 8 heads: 1018 us
   // against 1299 us for variant 57 and 1632 us for variant 15); the 9-tile

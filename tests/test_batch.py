@@ -77,10 +77,19 @@ def test_more_tiles_than_one_launch_holds():
 
 
 def test_general_family_batch():
-    # no rolling instantiation holds this window: every tile runs alone
+    # no rolling instantiation holds this window's halo at head dim 128:
+    # every tile runs alone
     dims = [(1, 22, 24, 24), (1, 20, 22, 23)]
-    plan = check_batch(dims, 1, 64, (19, 19, 19), 350, oracle_check=False)
+    plan = check_batch(dims, 1, 128, (19, 19, 19), 350, oracle_check=False)
     assert plan["launches"] == 2 and plan["variant"] == -1
+
+
+def test_four_group_window_batch():
+    # the same window at head dim 64: one shared launch of the four-group
+    # rolling instantiation
+    dims = [(1, 22, 24, 24), (1, 20, 22, 23)]
+    plan = check_batch(dims, 1, 64, (19, 19, 19), 355)
+    assert plan["launches"] == 1 and plan["variant"] >= 0
 
 
 def test_shared_inputs_and_given_outputs():

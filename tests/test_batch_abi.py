@@ -103,9 +103,10 @@ def test_plan_of_one_tile_matches_fwd():
 
 
 def test_plan_general_family_runs_tiles_alone():
-    # a window no rolling instantiation holds: every tile is its own launch
-    p = na.plan_batch([(1, 24, 24, 24), (1, 20, 20, 20)], 2, 64, (19, 19, 19))
-    assert na.plan((1, 24, 24, 24, 2, 64), (19, 19, 19))["family"] == 1
+    # a window whose halo no rolling instantiation's LDS holds at head dim
+    # 128: every tile is its own launch
+    p = na.plan_batch([(1, 24, 24, 24), (1, 20, 20, 20)], 2, 128, (19, 19, 19))
+    assert na.plan((1, 24, 24, 24, 2, 128), (19, 19, 19))["family"] == 1
     assert p["launches"] == 2 and p["shared_tiles"] == 0 and p["variant"] == -1
 
 

@@ -117,12 +117,20 @@ def test_large_window_full_grid():
     full_grid_check(w.shape, w.window, w.seed, "large_window (full grid)", w.k_outlier_frac)
 
 
-def test_general_family_workload_full_grid():
-    """The 19x19x19 workload (the general family's case: no rolling
-    instantiation holds its window union) at full size, every output."""
+def test_window_19_workload_full_grid():
+    """The 19x19x19 workload (the four-group rolling instantiation) at full
+    size, every output."""
     w = WORKLOADS["window_19"]
-    assert na.plan(w.shape, w.window)["family"] == 1
+    assert na.plan(w.shape, w.window)["family"] == 2
     full_grid_check(w.shape, w.window, w.seed, "window_19 (full grid)", w.k_outlier_frac)
+
+
+def test_general_family_workload_full_grid():
+    """The 19x19x19 workload at head dim 128 (the general family's case: no
+    rolling instantiation's LDS holds its halo) at full size, every output."""
+    w = WORKLOADS["window_19_hd128"]
+    assert na.plan(w.shape, w.window)["family"] == 1
+    full_grid_check(w.shape, w.window, w.seed, "window_19_hd128 (full grid)", w.k_outlier_frac)
 
 
 def test_full_scale_full_grid_streamed():
