@@ -132,7 +132,7 @@ struct Launch {
   X(14, 128, 2, 8, 2, 3, 1, 7, 1, 1, 0)        \
   X(15, 128, 2, 8, 1, 3, 1, 7, 2, 1, 0)        \
   X(16, 128, 4, 4, 1, 4, 1, 13, 1, 1, 0)       \
-  X(17, 256, 2, 8, 1, 3, 1, 7, 2, 1, 0)        \
+  X(17, 64, 2, 8, 2, 4, 1, 4, 1, 2, 4)         \
   X(18, 64, 2, 8, 4, 3, 1, 7, 1, 2, 0)         \
   X(19, 64, 4, 4, 4, 3, 1, 7, 1, 2, 0)         \
   X(20, 64, 2, 8, 1, 4, 1, 7, 1, 2, 0)         \

@@ -302,7 +302,10 @@ bool plan_roll(int v, const Geom& g, int tile_t, Launch* l, int target = kTarget
 int pick_roll(const Geom& g, Launch* l) {
   static const int p16[] = {11};
   static const int p32[] = {12};
-  static const int p64_small[] = {8, 34, 21, 26, 20, 9};       // union <= 64 keys
+  // union <= 64 keys: first the 8-wave two-buffer 4-tile variant (two 2x8
+  // blocks along H, four phases: 15-22% faster than the 3-wave variant 8 on
+  // the narrow edge tiles, 16x64x96 (3,3,3) and (3,5,3), 8x32x48 (3,3,5))
+  static const int p64_small[] = {17, 8, 34, 21, 26, 20, 9};
   static const int p64_mid[] = {42, 43, 40, 38, 35, 26, 34, 21, 20, 1, 9, 10};  // <= 112 keys
   // larger windows: 4x4 blocks for near-cubic ones; 2x8 blocks for windows
   // much wider along W (their union is smaller in 2x8 blocks), with one

@@ -292,6 +292,7 @@ def variant_cases():
              64: ((2, 9, 13, 21, 2, 64), (3, 7, 7)), 128: ((1, 7, 11, 19, 2, 128), (3, 7, 7)),
              256: ((1, 5, 9, 17, 1, 256), (3, 5, 5))}
     big = ((1, 12, 18, 22, 2, 64), (11, 11, 11))
+    small = ((1, 9, 13, 21, 2, 64), (3, 3, 5))  # unions of at most 4 tiles
     import ctypes
     lib = na.load()
     for var in range(na.num_variants()):
@@ -299,6 +300,10 @@ def variant_cases():
             buf = (ctypes.c_int * 10)()
             if lib.na3d_plan_config(*shape, *ks, 2, var, 0, buf) == 0:
                 cases.append((2, var, shape, ks))
+        if na.variant_info(var)["hd"] == 64 and na.variant_info(var)["nk"] * na.variant_info(var)["ng"] <= 4:
+            buf = (ctypes.c_int * 10)()
+            if lib.na3d_plan_config(*small[0], *small[1], 2, var, 0, buf) == 0:
+                cases.append((2, var) + small)
         buf = (ctypes.c_int * 10)()
         if lib.na3d_plan_config(*big[0], *big[1], 2, var, 0, buf) == 0:
             cases.append((2, var) + big)
