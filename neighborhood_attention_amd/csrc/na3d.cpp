@@ -328,6 +328,13 @@ int pick_roll(const Geom& g, Launch* l) {
   // on 16x64x96, 4 heads, (3,7,7))
   static const int p256[] = {53, 52};
   const int un28 = std::min(2 + g.KH - 1, g.H) * std::min(8 + g.KW - 1, g.W);
+  const int un44 = std::min(4 + g.KH - 1, g.H) * std::min(4 + g.KW - 1, g.W);
+  // head dim 64, windows whose 4x4-block union fits 4 tiles but whose 2x8
+  // union does not (e.g. (3,5,5): 64 against 72 keys): 4x4 blocks in 8-wave
+  // two-buffer workgroups with 4-tile groups, where the 2x8 choice would read
+  // 7 tiles (36x64x96 at 8 heads 272 against 293 us, at 32 heads 914
+  // against 1106 us; 16x64x96 at 8 heads 122 against 135 us)
+  if (g.HD == 64 && un28 > 64 && un44 <= 64 && plan_roll(63, g, 0, l)) return 1;
   const int* pref;
   int np;
   switch (g.HD) {
