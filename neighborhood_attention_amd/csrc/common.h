@@ -178,7 +178,8 @@ struct Launch {
   X(60, 128, 2, 4, 2, 2, 1, 11, 1, 1, 0) \
   X(61, 128, 2, 4, 4, 2, 1, 5, 1, 2, 0) \
   X(62, 64, 4, 4, 2, 4, 1, 8, 4, 1, 0) \
-  X(63, 64, 4, 4, 2, 4, 1, 4, 1, 2, 4)
+  X(63, 64, 4, 4, 2, 4, 1, 4, 1, 2, 4) \
+  X(64, 64, 2, 8, 2, 4, 1, 2, 1, 2, 4)
 
 struct RollVariant {
   int hd, qh, qw, wh, wt, ns, nk, ng, nbuf, occ;

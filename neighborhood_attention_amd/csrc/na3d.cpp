@@ -335,6 +335,10 @@ int pick_roll(const Geom& g, Launch* l) {
   // 7 tiles (36x64x96 at 8 heads 272 against 293 us, at 32 heads 914
   // against 1106 us; 16x64x96 at 8 heads 122 against 135 us)
   if (g.HD == 64 && un28 > 64 && un44 <= 64 && plan_roll(63, g, 0, l)) return 1;
+  // head dim 64, 2x8-block unions of at most 2 tiles (the W = 5 edge tile
+  // with (3,5,5): 6x5 = 30 keys): the same 8-wave shape with 2-tile groups
+  // (14.0 against 15.9 us for the 4-tile one)
+  if (g.HD == 64 && un28 <= 32 && plan_roll(64, g, 0, l)) return 1;
   const int* pref;
   int np;
   switch (g.HD) {

@@ -293,6 +293,7 @@ def variant_cases():
              256: ((1, 5, 9, 17, 1, 256), (3, 5, 5))}
     big = ((1, 12, 18, 22, 2, 64), (11, 11, 11))
     small = ((1, 9, 13, 21, 2, 64), (3, 3, 5))  # unions of at most 4 tiles
+    narrow = ((1, 9, 13, 5, 2, 64), (3, 3, 3))  # and of at most 2
     import ctypes
     lib = na.load()
     for var in range(na.num_variants()):
@@ -300,10 +301,12 @@ def variant_cases():
             buf = (ctypes.c_int * 10)()
             if lib.na3d_plan_config(*shape, *ks, 2, var, 0, buf) == 0:
                 cases.append((2, var, shape, ks))
-        if na.variant_info(var)["hd"] == 64 and na.variant_info(var)["nk"] * na.variant_info(var)["ng"] <= 4:
+        info = na.variant_info(var)
+        if info["hd"] == 64 and info["nk"] * info["ng"] <= 4:
+            sh = narrow if info["nk"] * info["ng"] <= 2 else small
             buf = (ctypes.c_int * 10)()
-            if lib.na3d_plan_config(*small[0], *small[1], 2, var, 0, buf) == 0:
-                cases.append((2, var) + small)
+            if lib.na3d_plan_config(*sh[0], *sh[1], 2, var, 0, buf) == 0:
+                cases.append((2, var) + sh)
         buf = (ctypes.c_int * 10)()
         if lib.na3d_plan_config(*big[0], *big[1], 2, var, 0, buf) == 0:
             cases.append((2, var) + big)
