@@ -179,7 +179,12 @@ struct Launch {
   X(61, 128, 2, 4, 4, 2, 1, 5, 1, 2, 0) \
   X(62, 64, 4, 4, 2, 4, 1, 8, 4, 1, 0) \
   X(63, 64, 4, 4, 2, 4, 1, 4, 1, 2, 4) \
-  X(64, 64, 2, 8, 2, 4, 1, 2, 1, 2, 4)
+  X(64, 64, 2, 8, 2, 4, 1, 2, 1, 2, 4) \
+  X(65, 32, 4, 4, 1, 4, 1, 13, 1, 1, 0) \
+  X(66, 32, 2, 8, 1, 4, 1, 13, 1, 1, 0) \
+  X(67, 32, 4, 4, 2, 4, 1, 8, 4, 1, 0) \
+  X(68, 32, 2, 8, 2, 4, 1, 7, 1, 2, 4) \
+  X(69, 32, 2, 4, 2, 2, 1, 11, 1, 1, 0)
 
 struct RollVariant {
   int hd, qh, qw, wh, wt, ns, nk, ng, nbuf, occ;

@@ -301,7 +301,15 @@ bool plan_roll(int v, const Geom& g, int tile_t, Launch* l, int target = kTarget
 // whose static limits fit the sizes wins.
 int pick_roll(const Geom& g, Launch* l) {
   static const int p16[] = {11};
-  static const int p32[] = {12};
+  // head dim 32: the head-dim-64 shapes (decoder-class 8-wave two-buffer
+  // 7-tile groups; 13-tile 4x4 and 2x8 one-group; four 8-tile groups), then
+  // the 2x8 two-group catch-all (16x64x96 (3,7,7) at 8 heads 105 against
+  // 267 us for the catch-all; 16x48x64 (11,11,11) 253 against 434 us, and
+  // 225 us on two-plane blocks (69, by the rule below); (3,5,27) on 4x8x128 at
+  // 32 heads 40 against 68 us; 24x32x32 (19,19,19) 300 against 1446 us on
+  // the general family)
+  static const int p32_mid[] = {68, 12};
+  static const int p32_large[] = {65, 66, 12, 67};
   // union <= 64 keys: first the 8-wave two-buffer 4-tile variant (two 2x8
   // blocks along H, four phases: 15-22% faster than the 3-wave variant 8 on
   // the narrow edge tiles, 16x64x96 (3,3,3) and (3,5,3), 8x32x48 (3,3,5))
@@ -343,7 +351,13 @@ int pick_roll(const Geom& g, Launch* l) {
   int np;
   switch (g.HD) {
     case 16: pref = p16; np = 1; break;
-    case 32: pref = p32; np = 1; break;
+    case 32:
+      if (un28 <= 112) {
+        pref = p32_mid; np = (int)(sizeof(p32_mid) / sizeof(int));
+      } else {
+        pref = p32_large; np = (int)(sizeof(p32_large) / sizeof(int));
+      }
+      break;
     case 64:
       if (un28 <= 64) {
         pref = p64_small; np = (int)(sizeof(p64_small) / sizeof(int));
@@ -388,7 +402,7 @@ int pick_roll(const Geom& g, Launch* l) {
     // queries against KT x the chosen variant's, by at least 5% (11x11x11:
     // 3% faster at head dim 64 on 16x48x64, 6% on 16x80x32 at 32 heads, 7%
     // at head dim 128)
-    const int pp = g.HD == 64 ? 59 : (g.HD == 128 ? 60 : -1);
+    const int pp = g.HD == 64 ? 59 : (g.HD == 128 ? 60 : (g.HD == 32 ? 69 : -1));
     if (pp >= 0 && g.KT >= 6) {
       const RollVariant& a = kRollVariants[l->variant];
       const RollVariant& c = kRollVariants[pp];

@@ -389,6 +389,8 @@ SPIKE_CASES = [
      [(0, 0, 0, 100), (4, 8, 12, 40), (7, 15, 23, 200), (2, 3, 20, 30)]),
     ((1, 8, 16, 40, 2, 64), (3, 5, 35),
      [(0, 0, 0, 100), (4, 8, 20, 45), (7, 15, 39, 250)]),
+    ((1, 12, 20, 24, 2, 32), (11, 11, 11),
+     [(0, 0, 0, 100), (6, 10, 12, 40), (3, 15, 5, 200), (9, 2, 20, 30)]),
 ]
 
 
@@ -408,12 +410,12 @@ def test_extreme_scores(shape, ks, spikes):
 
 
 def spike_variant_cases():
-    """Every rolling instantiation that plans the 11x11x11 (HD 64 and 128) or
-    3x5x27 spike grids."""
+    """Every rolling instantiation that plans the 11x11x11 (HD 32, 64 and
+    128) or 3x5x27 spike grids."""
     import ctypes
     lib = na.load()
     cases = []
-    for shape, ks, spikes in SPIKE_CASES[:3]:
+    for shape, ks, spikes in SPIKE_CASES[:3] + SPIKE_CASES[5:]:
         for var in range(na.num_variants()):
             buf = (ctypes.c_int * 10)()
             if lib.na3d_plan_config(*shape, *ks, 2, var, 0, buf) == 0:
