@@ -184,7 +184,12 @@ struct Launch {
   X(66, 32, 2, 8, 1, 4, 1, 13, 1, 1, 0) \
   X(67, 32, 4, 4, 2, 4, 1, 8, 4, 1, 0) \
   X(68, 32, 2, 8, 2, 4, 1, 7, 1, 2, 4) \
-  X(69, 32, 2, 4, 2, 2, 1, 11, 1, 1, 0)
+  X(69, 32, 2, 4, 2, 2, 1, 11, 1, 1, 0) \
+  X(70, 16, 4, 4, 1, 4, 1, 13, 1, 1, 0) \
+  X(71, 16, 2, 8, 1, 4, 1, 13, 1, 1, 0) \
+  X(72, 16, 4, 4, 2, 4, 1, 8, 4, 1, 0) \
+  X(73, 16, 2, 8, 2, 4, 1, 7, 1, 2, 4) \
+  X(74, 16, 2, 4, 2, 2, 1, 11, 1, 1, 0)
 
 struct RollVariant {
   int hd, qh, qw, wh, wt, ns, nk, ng, nbuf, occ;

@@ -300,7 +300,12 @@ bool plan_roll(int v, const Geom& g, int tile_t, Launch* l, int target = kTarget
 // head dimension and by the union of one 2x8 query block's windows; the first
 // whose static limits fit the sizes wins.
 int pick_roll(const Geom& g, Launch* l) {
-  static const int p16[] = {11};
+  // head dim 16: the same shapes as head dim 32 (16x64x96 (3,7,7) at 8 heads
+  // 105 against 186 us; 11x11x11 233 us on 4x4 blocks and 224 us on
+  // two-plane ones against 335 us; (3,5,27) at 32 heads 37 against 50 us;
+  // (19,19,19) 307 against 1347 us on the general family)
+  static const int p16_mid[] = {73, 11};
+  static const int p16_large[] = {70, 71, 11, 72};
   // head dim 32: the head-dim-64 shapes (decoder-class 8-wave two-buffer
   // 7-tile groups; 13-tile 4x4 and 2x8 one-group; four 8-tile groups), then
   // the 2x8 two-group catch-all (16x64x96 (3,7,7) at 8 heads 105 against
@@ -350,7 +355,13 @@ int pick_roll(const Geom& g, Launch* l) {
   const int* pref;
   int np;
   switch (g.HD) {
-    case 16: pref = p16; np = 1; break;
+    case 16:
+      if (un28 <= 112) {
+        pref = p16_mid; np = (int)(sizeof(p16_mid) / sizeof(int));
+      } else {
+        pref = p16_large; np = (int)(sizeof(p16_large) / sizeof(int));
+      }
+      break;
     case 32:
       if (un28 <= 112) {
         pref = p32_mid; np = (int)(sizeof(p32_mid) / sizeof(int));
@@ -402,7 +413,7 @@ int pick_roll(const Geom& g, Launch* l) {
     // queries against KT x the chosen variant's, by at least 5% (11x11x11:
     // 3% faster at head dim 64 on 16x48x64, 6% on 16x80x32 at 32 heads, 7%
     // at head dim 128)
-    const int pp = g.HD == 64 ? 59 : (g.HD == 128 ? 60 : (g.HD == 32 ? 69 : -1));
+    const int pp = g.HD == 64 ? 59 : g.HD == 128 ? 60 : g.HD == 32 ? 69 : g.HD == 16 ? 74 : -1;
     if (pp >= 0 && g.KT >= 6) {
       const RollVariant& a = kRollVariants[l->variant];
       const RollVariant& c = kRollVariants[pp];
