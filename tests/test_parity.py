@@ -249,6 +249,44 @@ def test_run_to_run_bitwise_deterministic():
     assert torch.equal(a, b)
 
 
+def test_concurrent_host_threads():
+    """Calls from several host threads at once, each on its own stream, with
+    plans of different instantiations (some above 64 KB of LDS) made for the
+    first time inside the threads: every result bitwise equal to the same call
+    made alone (the plan cache and the per-kernel LDS limits are shared
+    process state)."""
+    import threading
+    cases = [((1, 6, 20, 24, 2, 64), (3, 7, 7)), ((1, 12, 14, 18, 1, 64), (11, 11, 11)),
+             ((1, 5, 16, 21, 2, 128), (3, 7, 7)), ((1, 6, 13, 9, 2, 32), (3, 5, 5)),
+             ((1, 6, 18, 18, 1, 64), (5, 17, 17)), ((1, 4, 9, 7, 2, 64), (3, 5, 5))]
+    ins = [inputs_on_gpu(sh, 1100 + i) for i, (sh, _) in enumerate(cases)]
+    outs = [[torch.empty_like(q) for _ in range(3)] for q, _, _ in ins]
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for rep in range(3):
+                    q, k, v = ins[i]
+                    na.fwd(q, k, v, cases[i][1], out=outs[i][rep])
+            s.synchronize()
+        except Exception as e:  # reported below, in the main thread
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, ((sh, ks), (q, k, v)) in enumerate(zip(cases, ins)):
+        alone = run(q, k, v, ks)
+        for rep in range(3):
+            assert torch.equal(outs[i][rep], alone), (sh, ks, rep)
+
+
 def test_side_stream_and_aliased_inputs():
     q, _, _ = inputs_on_gpu((1, 4, 12, 16, 2, 32), 9)
     s = torch.cuda.Stream()
