@@ -946,7 +946,16 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
           if (pend_on && pend_ok) store_out<MT>(pend_p, ooff_pt, pend, g);
 #pragma unroll
           for (int s = 0; s < NS; ++s)
-            if (s == sl) pack_out<HD>(S[s], pend);
+            if (s == sl) {
+              // an empty asm on the accumulators keeps the normalisation here,
+              // on the retiring step: hoisted out of this branch, the compiler
+              // ran it on every step, waiting each time for the step's P.V
+              // MFMAs to land before the wave could go on to the barrier
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) asm volatile("" : "+v"(S[s].acc[mt]));
+              asm volatile("" : "+v"(S[s].accl));
+              pack_out<HD>(S[s], pend);
+            }
           pend_p = obase + (int64_t)tq(jlo) * a.so.t;
           pend_ok = qvalid && tq(jlo) + pt < t1;
           pend_on = true;
