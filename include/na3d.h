@@ -311,7 +311,9 @@ int na3d_num_variants(void);
  *   info: host array of 10 ints, written on success: [0] head dim, [1] QH
  *         and [2] QW, the query block on one plane (16 / (QH*QW) consecutive
  *         query planes per block, 1 or 2), [3] WH block rows and [4] WT
- *         query-plane phases per workgroup (WH*WT waves of 64 lanes), [5]
+ *         query-plane phases per workgroup (WH*WT computing waves of 64
+ *         lanes; some instantiations add waves that only stage K/V, which
+ *         the thread count of na3d_plan_config includes), [5]
  *         query-plane slots per wave, [6] 16-key tiles per softmax group, [7]
  *         groups, [8] staged plane buffers (1 or 2), [9] waves per SIMD the
  *         register allocation is capped for (0 = no cap).

@@ -111,93 +111,96 @@ struct Launch {
 // Instantiations of the rolling family: index, head dim, query block
 // (QH x QW queries of 16 / (QH x QW) consecutive query planes: 16 queries per
 // wave), wave grid (WH block rows x WT query-plane phases), query-plane slots per wave, 16-key tiles per softmax group, most
-// groups a wave's window union may need, staged plane buffers (1 or 2), and
-// the waves per SIMD the register allocation must leave room for (0 = the
-// compiler's choice; 4 caps it at 128 VGPRs).
+// groups a wave's window union may need, staged plane buffers (1 or 2), the
+// waves per SIMD the register allocation must leave room for (0 = the
+// compiler's choice; 4 caps it at 128 VGPRs), and staging waves (0: the
+// compute waves stage the K/V planes themselves; otherwise that many extra
+// waves per workgroup do nothing but stage them).
 #define NA3D_ROLL_VARIANTS(X)               \
-  X(0, 64, 2, 8, 1, 3, 1, 7, 1, 2, 0)          \
-  X(1, 64, 2, 8, 2, 3, 1, 7, 1, 2, 0)          \
-  X(2, 64, 4, 4, 2, 3, 1, 7, 1, 2, 0)          \
-  X(3, 64, 2, 8, 4, 3, 1, 7, 1, 1, 0)          \
-  X(4, 64, 2, 8, 2, 3, 1, 7, 1, 1, 0)          \
-  X(5, 64, 4, 4, 1, 4, 1, 13, 1, 1, 0)         \
-  X(6, 64, 4, 4, 1, 8, 1, 13, 1, 1, 0)         \
-  X(7, 64, 4, 4, 2, 4, 1, 13, 1, 1, 0)         \
-  X(8, 64, 2, 8, 1, 3, 1, 4, 1, 2, 0)          \
-  X(9, 64, 2, 8, 1, 3, 1, 7, 2, 2, 0)          \
-  X(10, 64, 4, 4, 1, 4, 1, 13, 2, 1, 0)        \
-  X(11, 16, 2, 8, 1, 3, 1, 7, 2, 2, 0)         \
-  X(12, 32, 2, 8, 1, 3, 1, 7, 2, 2, 0)         \
-  X(13, 128, 2, 8, 1, 3, 1, 7, 1, 2, 0)        \
-  X(14, 128, 2, 8, 2, 3, 1, 7, 1, 1, 0)        \
-  X(15, 128, 2, 8, 1, 3, 1, 7, 2, 1, 0)        \
-  X(16, 128, 4, 4, 1, 4, 1, 13, 1, 1, 0)       \
-  X(17, 64, 2, 8, 2, 4, 1, 4, 1, 2, 4)         \
-  X(18, 64, 2, 8, 4, 3, 1, 7, 1, 2, 0)         \
-  X(19, 64, 4, 4, 4, 3, 1, 7, 1, 2, 0)         \
-  X(20, 64, 2, 8, 1, 4, 1, 7, 1, 2, 0)         \
-  X(21, 64, 2, 8, 1, 4, 1, 7, 1, 1, 0)         \
-  X(22, 64, 4, 4, 1, 4, 1, 7, 2, 1, 0)         \
-  X(23, 64, 4, 4, 1, 4, 1, 7, 2, 2, 0)         \
-  X(24, 64, 4, 4, 2, 4, 1, 7, 2, 1, 0)         \
-  X(25, 128, 2, 8, 1, 4, 1, 7, 1, 1, 0)        \
-  X(26, 64, 2, 8, 2, 2, 2, 7, 1, 2, 0)         \
-  X(27, 64, 2, 8, 4, 1, 3, 4, 2, 1, 0)         \
-  X(28, 64, 2, 8, 2, 1, 3, 4, 2, 2, 0)         \
-  X(29, 128, 2, 8, 2, 2, 2, 4, 2, 1, 0)        \
-  X(30, 64, 2, 8, 1, 4, 1, 4, 2, 1, 0)         \
-  X(31, 64, 2, 8, 1, 4, 1, 4, 2, 2, 0)         \
-  X(32, 64, 4, 4, 1, 4, 1, 4, 2, 1, 0)         \
-  X(33, 128, 2, 8, 1, 4, 1, 4, 2, 1, 0) \
-  X(34, 64, 2, 8, 1, 4, 1, 7, 1, 1, 4)  \
-  X(35, 64, 4, 4, 1, 4, 1, 4, 2, 1, 4)  \
-  X(36, 64, 2, 8, 1, 4, 1, 4, 2, 1, 4)  \
-  X(37, 64, 4, 4, 1, 4, 1, 7, 1, 1, 4)  \
-  X(38, 64, 4, 4, 2, 4, 1, 7, 1, 1, 4)  \
-  X(39, 64, 4, 4, 2, 4, 1, 4, 2, 1, 4)  \
-  X(40, 64, 2, 8, 2, 4, 1, 7, 1, 1, 4)  \
-  X(41, 64, 2, 8, 4, 4, 1, 7, 1, 1, 4)  \
-  X(42, 64, 2, 8, 2, 4, 1, 7, 1, 2, 4)  \
-  X(43, 64, 4, 4, 2, 4, 1, 7, 1, 2, 4)  \
-  X(44, 64, 4, 4, 4, 4, 1, 7, 1, 1, 4)  \
-  X(45, 64, 4, 4, 3, 4, 1, 13, 1, 1, 3) \
-  X(46, 64, 4, 4, 3, 4, 1, 13, 1, 2, 3) \
-  X(47, 128, 2, 8, 2, 4, 1, 7, 1, 2, 0) \
-  X(48, 128, 2, 8, 2, 4, 1, 7, 1, 1, 0) \
-  X(49, 64, 2, 8, 1, 4, 1, 13, 1, 1, 0) \
-  X(50, 64, 2, 8, 2, 4, 1, 13, 1, 1, 0) \
-  X(51, 64, 2, 8, 2, 4, 1, 13, 1, 2, 0) \
-  X(52, 256, 2, 8, 1, 4, 1, 7, 1, 1, 0) \
-  X(53, 256, 4, 4, 1, 4, 1, 7, 1, 1, 0) \
-  X(54, 64, 2, 8, 2, 4, 1, 9, 2, 1, 0) \
-  X(55, 64, 2, 8, 2, 4, 1, 7, 3, 1, 0) \
-  X(56, 64, 2, 8, 2, 4, 1, 7, 4, 1, 0) \
-  X(57, 128, 2, 8, 1, 4, 1, 9, 2, 1, 0) \
-  X(58, 64, 2, 8, 1, 4, 1, 9, 2, 1, 0) \
-  X(59, 64, 2, 4, 2, 2, 1, 11, 1, 1, 0) \
-  X(60, 128, 2, 4, 2, 2, 1, 11, 1, 1, 0) \
-  X(61, 128, 2, 4, 4, 2, 1, 5, 1, 2, 0) \
-  X(62, 64, 4, 4, 2, 4, 1, 8, 4, 1, 0) \
-  X(63, 64, 4, 4, 2, 4, 1, 4, 1, 2, 4) \
-  X(64, 64, 2, 8, 2, 4, 1, 2, 1, 2, 4) \
-  X(65, 32, 4, 4, 1, 4, 1, 13, 1, 1, 0) \
-  X(66, 32, 2, 8, 1, 4, 1, 13, 1, 1, 0) \
-  X(67, 32, 4, 4, 2, 4, 1, 8, 4, 1, 0) \
-  X(68, 32, 2, 8, 2, 4, 1, 7, 1, 2, 4) \
-  X(69, 32, 2, 4, 2, 2, 1, 11, 1, 1, 0) \
-  X(70, 16, 4, 4, 1, 4, 1, 13, 1, 1, 0) \
-  X(71, 16, 2, 8, 1, 4, 1, 13, 1, 1, 0) \
-  X(72, 16, 4, 4, 2, 4, 1, 8, 4, 1, 0) \
-  X(73, 16, 2, 8, 2, 4, 1, 7, 1, 2, 4) \
-  X(74, 16, 2, 4, 2, 2, 1, 11, 1, 1, 0)
+  X(0, 64, 2, 8, 1, 3, 1, 7, 1, 2, 0, 0)          \
+  X(1, 64, 2, 8, 2, 3, 1, 7, 1, 2, 0, 0)          \
+  X(2, 64, 4, 4, 2, 3, 1, 7, 1, 2, 0, 0)          \
+  X(3, 64, 2, 8, 4, 3, 1, 7, 1, 1, 0, 0)          \
+  X(4, 64, 2, 8, 2, 3, 1, 7, 1, 1, 0, 0)          \
+  X(5, 64, 4, 4, 1, 4, 1, 13, 1, 1, 0, 0)         \
+  X(6, 64, 4, 4, 1, 8, 1, 13, 1, 1, 0, 0)         \
+  X(7, 64, 4, 4, 2, 4, 1, 13, 1, 1, 0, 0)         \
+  X(8, 64, 2, 8, 1, 3, 1, 4, 1, 2, 0, 0)          \
+  X(9, 64, 2, 8, 1, 3, 1, 7, 2, 2, 0, 0)          \
+  X(10, 64, 4, 4, 1, 4, 1, 13, 2, 1, 0, 0)        \
+  X(11, 16, 2, 8, 1, 3, 1, 7, 2, 2, 0, 0)         \
+  X(12, 32, 2, 8, 1, 3, 1, 7, 2, 2, 0, 0)         \
+  X(13, 128, 2, 8, 1, 3, 1, 7, 1, 2, 0, 0)        \
+  X(14, 128, 2, 8, 2, 3, 1, 7, 1, 1, 0, 0)        \
+  X(15, 128, 2, 8, 1, 3, 1, 7, 2, 1, 0, 0)        \
+  X(16, 128, 4, 4, 1, 4, 1, 13, 1, 1, 0, 0)       \
+  X(17, 64, 2, 8, 2, 4, 1, 4, 1, 2, 4, 0)         \
+  X(18, 64, 2, 8, 4, 3, 1, 7, 1, 2, 0, 0)         \
+  X(19, 64, 4, 4, 4, 3, 1, 7, 1, 2, 0, 0)         \
+  X(20, 64, 2, 8, 1, 4, 1, 7, 1, 2, 0, 0)         \
+  X(21, 64, 2, 8, 1, 4, 1, 7, 1, 1, 0, 0)         \
+  X(22, 64, 4, 4, 1, 4, 1, 7, 2, 1, 0, 0)         \
+  X(23, 64, 4, 4, 1, 4, 1, 7, 2, 2, 0, 0)         \
+  X(24, 64, 4, 4, 2, 4, 1, 7, 2, 1, 0, 0)         \
+  X(25, 128, 2, 8, 1, 4, 1, 7, 1, 1, 0, 0)        \
+  X(26, 64, 2, 8, 2, 2, 2, 7, 1, 2, 0, 0)         \
+  X(27, 64, 2, 8, 4, 1, 3, 4, 2, 1, 0, 0)         \
+  X(28, 64, 2, 8, 2, 1, 3, 4, 2, 2, 0, 0)         \
+  X(29, 128, 2, 8, 2, 2, 2, 4, 2, 1, 0, 0)        \
+  X(30, 64, 2, 8, 1, 4, 1, 4, 2, 1, 0, 0)         \
+  X(31, 64, 2, 8, 1, 4, 1, 4, 2, 2, 0, 0)         \
+  X(32, 64, 4, 4, 1, 4, 1, 4, 2, 1, 0, 0)         \
+  X(33, 128, 2, 8, 1, 4, 1, 4, 2, 1, 0, 0) \
+  X(34, 64, 2, 8, 1, 4, 1, 7, 1, 1, 4, 0)  \
+  X(35, 64, 4, 4, 1, 4, 1, 4, 2, 1, 4, 0)  \
+  X(36, 64, 2, 8, 1, 4, 1, 4, 2, 1, 4, 0)  \
+  X(37, 64, 4, 4, 1, 4, 1, 7, 1, 1, 4, 0)  \
+  X(38, 64, 4, 4, 2, 4, 1, 7, 1, 1, 4, 0)  \
+  X(39, 64, 4, 4, 2, 4, 1, 4, 2, 1, 4, 0)  \
+  X(40, 64, 2, 8, 2, 4, 1, 7, 1, 1, 4, 0)  \
+  X(41, 64, 2, 8, 4, 4, 1, 7, 1, 1, 4, 0)  \
+  X(42, 64, 2, 8, 2, 4, 1, 7, 1, 2, 4, 0)  \
+  X(43, 64, 4, 4, 2, 4, 1, 7, 1, 2, 4, 0)  \
+  X(44, 64, 4, 4, 4, 4, 1, 7, 1, 1, 4, 0)  \
+  X(45, 64, 4, 4, 3, 4, 1, 13, 1, 1, 3, 0) \
+  X(46, 64, 4, 4, 3, 4, 1, 13, 1, 2, 3, 0) \
+  X(47, 128, 2, 8, 2, 4, 1, 7, 1, 2, 0, 0) \
+  X(48, 128, 2, 8, 2, 4, 1, 7, 1, 1, 0, 0) \
+  X(49, 64, 2, 8, 1, 4, 1, 13, 1, 1, 0, 0) \
+  X(50, 64, 2, 8, 2, 4, 1, 13, 1, 1, 0, 0) \
+  X(51, 64, 2, 8, 2, 4, 1, 13, 1, 2, 0, 0) \
+  X(52, 256, 2, 8, 1, 4, 1, 7, 1, 1, 0, 0) \
+  X(53, 256, 4, 4, 1, 4, 1, 7, 1, 1, 0, 0) \
+  X(54, 64, 2, 8, 2, 4, 1, 9, 2, 1, 0, 0) \
+  X(55, 64, 2, 8, 2, 4, 1, 7, 3, 1, 0, 0) \
+  X(56, 64, 2, 8, 2, 4, 1, 7, 4, 1, 0, 0) \
+  X(57, 128, 2, 8, 1, 4, 1, 9, 2, 1, 0, 0) \
+  X(58, 64, 2, 8, 1, 4, 1, 9, 2, 1, 0, 0) \
+  X(59, 64, 2, 4, 2, 2, 1, 11, 1, 1, 0, 0) \
+  X(60, 128, 2, 4, 2, 2, 1, 11, 1, 1, 0, 0) \
+  X(61, 128, 2, 4, 4, 2, 1, 5, 1, 2, 0, 0) \
+  X(62, 64, 4, 4, 2, 4, 1, 8, 4, 1, 0, 0) \
+  X(63, 64, 4, 4, 2, 4, 1, 4, 1, 2, 4, 0) \
+  X(64, 64, 2, 8, 2, 4, 1, 2, 1, 2, 4, 0) \
+  X(65, 32, 4, 4, 1, 4, 1, 13, 1, 1, 0, 0) \
+  X(66, 32, 2, 8, 1, 4, 1, 13, 1, 1, 0, 0) \
+  X(67, 32, 4, 4, 2, 4, 1, 8, 4, 1, 0, 0) \
+  X(68, 32, 2, 8, 2, 4, 1, 7, 1, 2, 4, 0) \
+  X(69, 32, 2, 4, 2, 2, 1, 11, 1, 1, 0, 0) \
+  X(70, 16, 4, 4, 1, 4, 1, 13, 1, 1, 0, 0) \
+  X(71, 16, 2, 8, 1, 4, 1, 13, 1, 1, 0, 0) \
+  X(72, 16, 4, 4, 2, 4, 1, 8, 4, 1, 0, 0) \
+  X(73, 16, 2, 8, 2, 4, 1, 7, 1, 2, 4, 0) \
+  X(74, 16, 2, 4, 2, 2, 1, 11, 1, 1, 0, 0) \
+  X(75, 128, 2, 4, 4, 2, 1, 5, 1, 2, 3, 4)
 
 struct RollVariant {
-  int hd, qh, qw, wh, wt, ns, nk, ng, nbuf, occ;
+  int hd, qh, qw, wh, wt, ns, nk, ng, nbuf, occ, pw;
 };
 
 constexpr RollVariant kRollVariants[] = {
-#define NA3D_ROLL_ENTRY(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC) \
-  {HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC},
+#define NA3D_ROLL_ENTRY(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW) \
+  {HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW},
     NA3D_ROLL_VARIANTS(NA3D_ROLL_ENTRY)
 #undef NA3D_ROLL_ENTRY
 };

@@ -284,7 +284,7 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
 
 // The whole kernel for workgroup `wg` of the problem in `a` (one grid, or
 // one tile of a batch).
-template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC, int PW>
 __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   // A wave owns 16 queries: a QH x QW block of PT consecutive query planes
   // (PT = 2 for 8-query spatial blocks: the union of their windows is
@@ -298,7 +298,14 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   constexpr int CPR = HD / 8;  // 16-byte chunks per staged row
   constexpr int RB = HD * 2;   // staged row bytes
   constexpr int BH = WH * QH;
-  constexpr int NT = kWave * WH * WT;
+  // With PW > 0 the workgroup has PW staging waves after its WH x WT compute
+  // waves: they issue every K/V plane's loads and compute nothing, so the
+  // compute waves never wait behind the plane's burst of loads at the CU's
+  // address unit (with one workgroup per CU, every wave otherwise spends a
+  // large part of each step there).  NT = the threads that stage.
+  constexpr int NTC = kWave * WH * WT;
+  constexpr int NT = PW > 0 ? kWave * PW : NTC;
+  constexpr int NTA = NTC + kWave * PW;
   constexpr int RSTEP = NT / CPR;  // staged rows per DMA round
   constexpr int GK = 16 * NK;      // keys per softmax group
   constexpr int NP = NK / 2;       // 32-key tile pairs per group
@@ -325,8 +332,13 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   const int lane = tid % kWave;
   const int q16 = lane & 15;
   const int g = lane >> 4;
+  const bool stager = PW > 0 && wave >= WH * WT;  // a staging wave
+  const bool computes = !stager;
   const int ih = wave % WH;
   const int it = wave / WH;
+  // the thread's (and wave's) place among the threads that stage
+  const int stid = PW > 0 ? tid - NTC : tid;
+  const int swave = PW > 0 ? wave - WH * WT : wave;
 
   // ---- workgroup -> (b, n, tile_h, tile_w, run group); run groups vary
   // fastest.  Within a head the spatial tiles are visited in bands of band_h
@@ -384,7 +396,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
 
   // ---- this wave's block of 16 queries
   const int bh0 = h0 + ih * QH;
-  const bool active = bh0 < Hq;
+  const bool active = computes && bh0 < Hq;
   const int pt = q16 / BQ;  // this lane's plane within the block (PT > 1)
   const int qr = q16 % BQ;  // and its query within that plane's block
   const int qh = bh0 + qr / QW;
@@ -533,8 +545,8 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   // wave lands at chunk P of the buffer (row P / CPR, physical chunk P % CPR).
   // A thread's source offsets (bytes within a plane) advance by RSTEP halo
   // rows per round; they are the same for every plane.
-  const int pc = tid % CPR;
-  const int row0 = tid / CPR;
+  const int pc = stid % CPR;
+  const int row0 = stid / CPR;
   const int step_h = RSTEP / hwd, step_w = RSTEP % hwd;
   // byte steps of K/V along W and H (32-bit: the host keeps one head's
   // spatial plane below 4 GiB for this family; wrapping arithmetic is exact)
@@ -570,7 +582,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   auto issue_stage = [&](int tp, int bufi) {
     const uint16_t* kpl = kbase + (int64_t)tp * a.sk.t;
     const uint16_t* vpl = vbase + (int64_t)tp * a.sv.t;
-    const uint32_t dk = lds_addr(smem + bufi * 2 * buf_bytes + wave * kWave * 16);
+    const uint32_t dk = lds_addr(smem + bufi * 2 * buf_bytes + swave * kWave * 16);
     if constexpr (kWrapBits) {
       uint32_t d = d0s;
       int r = 0;
@@ -578,7 +590,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
         dma16_kv(kpl, vpl, d, dk + r * NT * 16, buf_bytes);
         d += dstep + (dwrap & (uint32_t)__builtin_amdgcn_sbfe((int)wbits, r, 1));
       }
-      if (r * NT + tid < total_chunks) dma16_kv(kpl, vpl, d, dk + r * NT * 16, buf_bytes);
+      if (r * NT + stid < total_chunks) dma16_kv(kpl, vpl, d, dk + r * NT * 16, buf_bytes);
       return;
     }
     uint32_t d = d0s;
@@ -598,7 +610,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
       dma16_kv(kpl, vpl, lane_ofs(), dk + r * NT * 16, buf_bytes);
       advance();
     }
-    if (r * NT + tid < total_chunks) dma16_kv(kpl, vpl, lane_ofs(), dk + r * NT * 16, buf_bytes);
+    if (r * NT + stid < total_chunks) dma16_kv(kpl, vpl, lane_ofs(), dk + r * NT * 16, buf_bytes);
   };
 
   // The same walk by a subset of the waves: the wave of rank `rank` among
@@ -607,7 +619,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   // flight at a key plane stage the next one while the others compute (the
   // compute of a key plane is long enough to cover the slower issue; at
   // smaller HD the plane then lands late and this measured slower).
-  constexpr bool kIdleStaging = NBUF == 2 && HD >= 128 && PT == 1;
+  constexpr bool kIdleStaging = NBUF == 2 && HD >= 128 && PT == 1 && PW == 0;
   auto issue_stage_by = [&](int tp, int bufi, int rank, int nst) {
     const uint16_t* kpl = kbase + (int64_t)tp * a.sk.t;
     const uint16_t* vpl = vbase + (int64_t)tp * a.sv.t;
@@ -637,7 +649,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   // masked keys); the first barrier of the stream orders these stores
   {
     const int pad16 = (a.lds_rows - halo_rows) * (RB / 16);
-    for (int i = tid; i < 2 * NBUF * pad16; i += NT) {
+    for (int i = tid; i < 2 * NBUF * pad16; i += NTA) {
       const int region = i / pad16;
       *reinterpret_cast<uint4*>(smem + region * buf_bytes + halo_rows * RB + (i - region * pad16) * 16) =
           make_uint4(0, 0, 0, 0);
@@ -665,7 +677,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   bool pend_ok = false;       // ... and whether this lane's query is stored
   int t0, t1;
   run_bounds(r_lo, t0, t1);
-  issue_stage(wst(t0), 0);  // step st uses buffer st % NBUF
+  if (PW == 0 || stager) issue_stage(wst(t0), 0);  // step st uses buffer st % NBUF
   int st = 0;
   for (int ri = r_lo; ri < r_hi; ++ri) {
     if (ri > r_lo) run_bounds(ri, t0, t1);
@@ -687,7 +699,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
         while (alo <= ahi && wst(alo) + KT - 1 < tp) ++alo;
       }
       // admit this wave's query planes whose window starts here
-      while (tq(jhi + 1) < t1 && wst(tq(jhi + 1)) <= tp) {
+      while (computes && tq(jhi + 1) < t1 && wst(tq(jhi + 1)) <= tp) {
         ++jhi;
         const int sl = jhi % NS;
 #pragma unroll
@@ -713,7 +725,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
       }
       const int nxt = tp + 1 < p1 ? tp + 1 : np0;  // plane of the next step, -1 = none
       if (NBUF == 2 && nxt >= 0 && !kIdleStaging) {
-        issue_stage(nxt, (st + 1) & 1);
+        if (PW == 0 || stager) issue_stage(nxt, (st + 1) & 1);
       } else if (NBUF == 2 && nxt >= 0) {
         // waves with nothing to compute at this key plane stage the next one
         // (all waves when none is idle): a wave of phase i is busy when one of
@@ -737,7 +749,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
         }
       }
       // fetch Q of the query plane (if any) this wave admits at the next step
-      {
+      if (computes) {
         int tn = -1;
         if (tp + 1 < p1) {
           if (tq(jhi + 1) < t1 && wst(tq(jhi + 1)) == tp + 1) tn = tq(jhi + 1);
@@ -965,17 +977,17 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
       // one buffer: every wave must be done with plane tp before it is refilled
       if (NBUF == 1 && nxt >= 0) {
         __syncthreads();
-        issue_stage(nxt, 0);
+        if (PW == 0 || stager) issue_stage(nxt, 0);
       }
     }
   }
   if (pend_on && pend_ok) store_out<MT>(pend_p, ooff_pt, pend, g);
 }
 
-template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
-__global__ void __launch_bounds__(kWave * WH * WT) __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1)))
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC, int PW>
+__global__ void __launch_bounds__(kWave * (WH * WT + PW)) __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1)))
 na3d_fwd_roll_kernel(const RollArgs a) {
-  roll_body<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>(a, xcd_remap(blockIdx.x, gridDim.x));
+  roll_body<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW>(a, xcd_remap(blockIdx.x, gridDim.x));
 }
 
 // Many grids in one launch: the launch's workgroups are the tiles' grids one
@@ -983,8 +995,8 @@ na3d_fwd_roll_kernel(const RollArgs a) {
 // is not after it) and runs that tile's problem exactly as a launch of that
 // tile alone would (same staging layout, so the same arithmetic), with the
 // window and heads shared by all tiles and LDS sized for the largest.
-template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
-__global__ void __launch_bounds__(kWave * WH * WT) __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1)))
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC, int PW>
+__global__ void __launch_bounds__(kWave * (WH * WT + PW)) __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1)))
 na3d_fwd_roll_batch_kernel(const RollArgs shared, const RollBatch bt) {
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   int i = 0;
@@ -1006,21 +1018,21 @@ na3d_fwd_roll_batch_kernel(const RollArgs shared, const RollBatch bt) {
   c.t = (int64_t)t.H * c.h;
   c.b = (int64_t)t.T * c.t;
   a.sq = a.sk = a.sv = a.so = c;
-  roll_body<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>(a, wg - t.wg_off);
+  roll_body<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW>(a, wg - t.wg_off);
 }
 
 // ------------------------------------------------------------------ launch
-template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC, int PW>
 int launch_cfg(const RollArgs& a, const Launch& l, hipStream_t stream) {
-  constexpr auto kern = na3d_fwd_roll_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>;
+  constexpr auto kern = na3d_fwd_roll_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW>;
   if (set_lds<kern>(l.lds_bytes) != 0) return -1;
   hipLaunchKernelGGL(kern, dim3((unsigned)l.wgs), dim3(l.threads), l.lds_bytes, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC>
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC, int PW>
 int launch_batch_cfg(const RollArgs& a, const RollBatch& bt, const Launch& l, hipStream_t stream) {
-  constexpr auto kern = na3d_fwd_roll_batch_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>;
+  constexpr auto kern = na3d_fwd_roll_batch_kernel<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW>;
   if (set_lds<kern>(l.lds_bytes) != 0) return -1;
   hipLaunchKernelGGL(kern, dim3((unsigned)l.wgs), dim3(l.threads), l.lds_bytes, stream, a, bt);
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -1051,8 +1063,8 @@ int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s) {
   a.so = p.so;
   if (l.variant < 0 || l.variant >= kNumRollVariants || kRollVariants[l.variant].hd != hd) return -1;
   switch (l.variant) {
-#define NA3D_ROLL_CASE(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC) \
-  case i: return launch_cfg<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>(a, l, s);
+#define NA3D_ROLL_CASE(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW) \
+  case i: return launch_cfg<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW>(a, l, s);
     NA3D_ROLL_VARIANTS(NA3D_ROLL_CASE)
 #undef NA3D_ROLL_CASE
     default: return -1;
@@ -1077,8 +1089,8 @@ int launch_roll_batch(const Problem& p, const Launch& l, const RollBatch& bt, in
   if (l.variant < 0 || l.variant >= kNumRollVariants || kRollVariants[l.variant].hd != hd) return -1;
   if (bt.n < 1 || bt.n > kMaxBatch) return -1;
   switch (l.variant) {
-#define NA3D_ROLL_BATCH_CASE(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC) \
-  case i: return launch_batch_cfg<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC>(a, bt, l, s);
+#define NA3D_ROLL_BATCH_CASE(i, HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW) \
+  case i: return launch_batch_cfg<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW>(a, bt, l, s);
     NA3D_ROLL_VARIANTS(NA3D_ROLL_BATCH_CASE)
 #undef NA3D_ROLL_BATCH_CASE
     default: return -1;

@@ -243,7 +243,10 @@ bool plan_roll(int v, const Geom& g, int tile_t, Launch* l, int target = kTarget
   if (lds > kMaxLdsBytes) return false;
   // the kernel's staging walk keeps one bit per full DMA round of a plane
   // (at most 32; the LDS limit above already bounds them by 27)
-  if ((int64_t)halo_max * (HD / 8) / (kWave * rv.wh * rv.wt) > 32) return false;
+  // (a round is one 16-byte chunk per staging lane: the compute waves', or
+  // the staging waves' where the variant has them)
+  const int stagers = kWave * (rv.pw > 0 ? rv.pw : rv.wh * rv.wt);
+  if ((int64_t)halo_max * (HD / 8) / stagers > 32) return false;
   const int tiles_h = ceil_div(g.box.Hq, BH), tiles_w = ceil_div(g.box.Wq, rv.qw);
   const int64_t spatial = (int64_t)g.B * g.NH * tiles_h * tiles_w;
   const TAxis ax{g.box.Tq, g.box.t0, g.T, g.KT};
@@ -279,7 +282,7 @@ bool plan_roll(int v, const Geom& g, int tile_t, Launch* l, int target = kTarget
   l->ta = r.ta;
   l->tz = r.tz;
   l->wgs = spatial * l->tiles_t;
-  l->threads = kWave * rv.wh * rv.wt;
+  l->threads = kWave * (rv.wh * rv.wt + rv.pw);
   l->lds_rows = rows;
   l->lds_bytes = (int)lds;
   l->planes = std::min(rpw, nruns) == 1 ? most : total;  // upper bound for run groups
@@ -387,7 +390,10 @@ int pick_roll(const Geom& g, Launch* l) {
   // wave works on every key plane, where 2x8 blocks on single planes leave
   // one phase in four idle): 4653 against 4952 us on the 32x128x192,
   // 16-head grid
-  if (g.HD == 128 && g.KT == 3 && plan_roll(61, g, 0, l)) return 1;
+  // The same blocks with four staging waves added to the workgroup (75): the
+  // compute waves no longer issue the plane's loads (4179 against 4591 us on
+  // the same grid)
+  if (g.HD == 128 && g.KT == 3 && (plan_roll(75, g, 0, l) || plan_roll(61, g, 0, l))) return 1;
   for (int i = 0; i < np; ++i) {
     if (!plan_roll(pref[i], g, 0, l)) continue;
     // windows much wider than tall, on a grid large enough that the 8-wave
