@@ -81,6 +81,37 @@ constexpr float kRealScore = -1.0e27f;    // scores below this are masked ones
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left free (gfx9 layout)
 constexpr int kWaitVm0 = 0x0f70;
 
+// Division of a 32-bit unsigned value by a divisor fixed for the launch,
+// by multiplication: the round-up method of Granlund and Montgomery
+// ("Division by invariant integers using multiplication", 1994, section 4).
+// With l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (the host
+// derives them), n / d = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0) with
+// t = mulhi(m, n), exact for every 32-bit n: a few scalar instructions where
+// a plain division of uniform values takes a reciprocal sequence on the
+// vector unit.  FAST = false divides plainly (the batch kernel, whose tiles
+// are described on the device).
+struct UDiv {
+  uint32_t d, m;
+  int s1, s2;
+};
+UDiv make_udiv(uint32_t d) {
+  UDiv v;
+  v.d = d;
+  int l = 0;
+  while (l < 32 && ((uint64_t)1 << l) < d) ++l;
+  v.m = (uint32_t)(((((uint64_t)1 << l) - d) << 32) / d + 1);
+  v.s1 = l < 1 ? l : 1;
+  v.s2 = l > 1 ? l - 1 : 0;
+  return v;
+}
+__host__ __device__ inline UDiv plain_udiv(uint32_t d) { return UDiv{d, 0u, 0, 0}; }
+template <bool FAST>
+__device__ __forceinline__ uint32_t udiv(uint32_t n, const UDiv& v) {
+  if constexpr (!FAST) return n / v.d;
+  const uint32_t t = __umulhi(v.m, n);
+  return (t + ((n - t) >> v.s1)) >> v.s2;
+}
+
 struct RollArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -99,6 +130,9 @@ struct RollArgs {
   int lds_rows;  // rows of each K and V staging buffer
   int band_h;    // spatial tiles are visited in bands of this many tile rows
   Strides sq, sk, sv, so;  // element strides; k and v share h, w and n
+  // the workgroup-index divisors: tiles_t, tiles_h * tiles_w, band_h *
+  // tiles_w, band_h, the last band's tile rows, NH
+  UDiv dv_tt, dv_nt, dv_br, dv_bh, dv_bl, dv_nh;
 };
 
 // Max over the 4 lanes (l, l^16, l^32, l^48) that hold one query,
@@ -284,7 +318,8 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
 
 // The whole kernel for workgroup `wg` of the problem in `a` (one grid, or
 // one tile of a batch).
-template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC, int PW>
+template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC, int PW,
+          bool FASTDIV>
 __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   // A wave owns 16 queries: a QH x QW block of PT consecutive query planes
   // (PT = 2 for 8-query spatial blocks: the union of their windows is
@@ -346,19 +381,19 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
   // the workgroups in flight on one XCD (consecutive indices, see xcd_remap)
   // cover a compact block of the grid and read the halo rows they share
   // from that XCD's L2 rather than from HBM.
-  const int tt = wg % a.tiles_t;
-  wg /= a.tiles_t;
+  const int wq1 = (int)udiv<FASTDIV>((uint32_t)wg, a.dv_tt);
+  const int tt = wg - wq1 * a.tiles_t;
   const int ntile = a.tiles_h * a.tiles_w;
-  const int j = wg % ntile;
-  wg /= ntile;
+  const int wq2 = (int)udiv<FASTDIV>((uint32_t)wq1, a.dv_nt);
+  const int j = wq1 - wq2 * ntile;
   const int band_rows = a.band_h * a.tiles_w;
-  const int band = j / band_rows;
+  const int band = (int)udiv<FASTDIV>((uint32_t)j, a.dv_br);
   const int jb = j - band * band_rows;
   const int gh = min(a.band_h, a.tiles_h - band * a.band_h);  // rows in this band
-  const int th = band * a.band_h + jb % gh;
-  const int tw = jb / gh;
-  const int n = wg % a.NH;
-  const int b = wg / a.NH;
+  const int tw = (int)udiv<FASTDIV>((uint32_t)jb, gh == a.band_h ? a.dv_bh : a.dv_bl);
+  const int th = band * a.band_h + jb - tw * gh;
+  const int b = (int)udiv<FASTDIV>((uint32_t)wq2, a.dv_nh);
+  const int n = wq2 - b * a.NH;
 
   const int T = a.T, H = a.H, W = a.W, KT = a.KT, KH = a.KH, KW = a.KW;
   const int Hq = a.Hq, Wq = a.Wq;
@@ -987,7 +1022,7 @@ __device__ __forceinline__ void roll_body(const RollArgs& a, int wg) {
 template <int HD, int QH, int QW, int WH, int WT, int NS, int NK, int NG, int NBUF, int OCC, int PW>
 __global__ void __launch_bounds__(kWave * (WH * WT + PW)) __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1)))
 na3d_fwd_roll_kernel(const RollArgs a) {
-  roll_body<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW>(a, xcd_remap(blockIdx.x, gridDim.x));
+  roll_body<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW, true>(a, xcd_remap(blockIdx.x, gridDim.x));
 }
 
 // Many grids in one launch: the launch's workgroups are the tiles' grids one
@@ -1011,6 +1046,12 @@ na3d_fwd_roll_batch_kernel(const RollArgs shared, const RollBatch bt) {
   a.tc = t.tc; a.ta = t.ta; a.tz = t.tz; a.nruns = t.nruns; a.rpw = t.rpw;
   a.lds_rows = t.lds_rows;
   a.band_h = 1;
+  a.dv_tt = plain_udiv((uint32_t)t.tiles_t);
+  a.dv_nt = plain_udiv((uint32_t)(t.tiles_h * t.tiles_w));
+  a.dv_br = plain_udiv((uint32_t)t.tiles_w);
+  a.dv_bh = plain_udiv(1u);
+  a.dv_bl = plain_udiv(1u);
+  a.dv_nh = plain_udiv((uint32_t)a.NH);
   Strides c;
   c.n = HD;
   c.w = (int64_t)a.NH * HD;
@@ -1018,7 +1059,7 @@ na3d_fwd_roll_batch_kernel(const RollArgs shared, const RollBatch bt) {
   c.t = (int64_t)t.H * c.h;
   c.b = (int64_t)t.T * c.t;
   a.sq = a.sk = a.sv = a.so = c;
-  roll_body<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW>(a, wg - t.wg_off);
+  roll_body<HD, QH, QW, WH, WT, NS, NK, NG, NBUF, OCC, PW, false>(a, wg - t.wg_off);
 }
 
 // ------------------------------------------------------------------ launch
@@ -1057,6 +1098,15 @@ int launch_roll(const Problem& p, const Launch& l, int hd, hipStream_t s) {
   a.rpw = l.rpw;
   a.lds_rows = l.lds_rows;
   a.band_h = l.band_h;
+  {
+    const int nbands = (l.tiles_h + l.band_h - 1) / l.band_h;
+    a.dv_tt = make_udiv((uint32_t)l.tiles_t);
+    a.dv_nt = make_udiv((uint32_t)(l.tiles_h * l.tiles_w));
+    a.dv_br = make_udiv((uint32_t)(l.band_h * l.tiles_w));
+    a.dv_bh = make_udiv((uint32_t)l.band_h);
+    a.dv_bl = make_udiv((uint32_t)(l.tiles_h - (nbands - 1) * l.band_h));
+    a.dv_nh = make_udiv((uint32_t)p.NH);
+  }
   a.sq = p.sq;
   a.sk = p.sk;
   a.sv = p.sv;
@@ -1086,6 +1136,7 @@ int launch_roll_batch(const Problem& p, const Launch& l, const RollBatch& bt, in
   a.lds_rows = l.lds_rows;
   a.band_h = 1;
   a.sq = a.sk = a.sv = a.so = Strides{0, 0, 0, 0, 0};
+  a.dv_tt = a.dv_nt = a.dv_br = a.dv_bh = a.dv_bl = a.dv_nh = plain_udiv(1u);  // set per tile
   if (l.variant < 0 || l.variant >= kNumRollVariants || kRollVariants[l.variant].hd != hd) return -1;
   if (bt.n < 1 || bt.n > kMaxBatch) return -1;
   switch (l.variant) {
