@@ -426,7 +426,17 @@ int pick_roll(const Geom& g, Launch* l) {
       const int64_t ca = (int64_t)(g.KT + 16 / (a.qh * a.qw) - 1) * a.ng * a.nk;
       const int64_t cc = (int64_t)(g.KT + 16 / (c.qh * c.qw) - 1) * c.ng * c.nk;
       Launch alt;
-      if (cc * 20 < ca * 19 && plan_roll(pp, g, 0, &alt)) *l = alt;
+      if (cc * 20 < ca * 19 && plan_roll(pp, g, 0, &alt)) {
+        *l = alt;
+        // head dim 64 on grids of 32 or more query planes: the same blocks
+        // in 12-wave workgroups of 12x4-query tiles (one per CU, two plane
+        // buffers), whose halo is re-read by 6.4 rather than 12.3 workgroups
+        // per query (11x11x11: 79x192x192 at 32 heads 80.7 against 107.0 ms,
+        // at 4 heads 10.25 against 10.72 ms; 40x96x96 at 32 heads 9.93
+        // against 10.53 ms; even on 32x96x96; slower on 16- and 24-plane
+        // grids, e.g. 16x48x64 at 8 heads 320 against 303 us)
+        if (pp == 59 && g.box.Tq >= 32 && plan_roll(76, g, 0, &alt)) *l = alt;
+      }
     }
     return 1;
   }

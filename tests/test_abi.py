@@ -152,3 +152,12 @@ def test_plan_covers_grid():
         assert 0 < p["lds_bytes"] <= 160 * 1024
     with pytest.raises(na.NA3DError):
         na.plan((1, 2, 2, 2, 1, 32), (3, 1, 1))
+
+
+def test_two_plane_tile_by_grid_length():
+    """11x11x11 at head dim 64: two-plane blocks in 4-wave workgroups of
+    4x4-query tiles on short grids, in 12-wave ones of 12x4-query tiles from
+    32 query planes on."""
+    for T, wh in [(16, 2), (24, 2), (32, 6), (79, 6)]:
+        info = na.variant_info(na.plan((1, T, 96, 96, 8, 64), (11, 11, 11))["variant"])
+        assert info["qh"] * info["qw"] == 8 and info["wh"] == wh, (T, info)

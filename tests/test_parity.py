@@ -177,6 +177,16 @@ def test_large_window_reduced_full_grid():
     full_grid_check((1, 12, 20, 24, 2, 64), (11, 11, 11), 41, "11x11x11 reduced grid")
 
 
+def test_long_grid_default_plan_full_grid():
+    """11x11x11 on a grid of 34 query planes: the default plan takes the
+    12-wave two-plane-block workgroups of 12x4-query tiles (ragged along T,
+    H and W), compared with the oracle on every output."""
+    shape, ks = (1, 34, 20, 26, 2, 64), (11, 11, 11)
+    info = na.variant_info(na.plan(shape, ks)["variant"])
+    assert info["qh"] * info["qw"] == 8 and info["wh"] == 6
+    full_grid_check(shape, ks, 43, "11x11x11 long grid, default plan")
+
+
 def test_full_scale_reduced_full_grid():
     full_grid_check((1, 6, 20, 30, 2, 128), (3, 7, 7), 51, "full-scale recipe reduced grid",
                     frac=0.01)
