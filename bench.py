@@ -44,6 +44,7 @@ NORM_SOURCES = ("neighborhood_attention_amd/csrc/common.h",
                 "neighborhood_attention_amd/csrc/kernel_rmsnorm.hip",
                 "neighborhood_attention_amd/csrc/na3d.cpp")
 NORM_EPS = 1e-6
+WARMUP_MIN_S = 0.05  # least wall time of warm-up launches before a timed region
 
 
 def parse():
@@ -105,22 +106,41 @@ def measured_traffic(workload, profile="na3d_fwd_roll_%s_traffic.md", sources=KE
     return float(tb.group(1))
 
 
-def time_kernel(fn, steps, warmup):
-    """Warm up, then time `steps` back-to-back launches.  Returns (wall ms per
-    step, kernel ms per launch from HIP events recorded on the stream the
-    kernel is launched on: torch's current stream, which fn uses)."""
+def warm_up(fn, warmup):
+    """At least `warmup` launches and at least WARMUP_MIN_S of them: the GPU
+    sits idle while the host checks parity, and its clocks take a few
+    milliseconds of work to come back up (a 50-launch decoder-tile region
+    measured 164 us per launch after 5 warm-up launches, 144 us after 200)."""
     import torch
 
-    for _ in range(warmup):
+    n = 0
+    t0 = time.perf_counter()
+    while n < warmup or time.perf_counter() - t0 < WARMUP_MIN_S:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    return n
+
+
+def time_kernel(fn, steps, warmup):
+    """Warm up (warm_up), then time `steps` back-to-back launches.  Returns
+    (wall ms per step, kernel ms per launch from HIP events recorded on the
+    stream the kernel is launched on: torch's current stream, which fn
+    uses)."""
+    import torch
+
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    # no garbage-collection pass of the host process inside the timed region
+    # no garbage-collection pass of the host process inside the timed region;
+    # the collection runs before the warm-up, so the GPU goes from the
+    # warm-up launches to the timed ones without an idle stretch between
     gc.collect()
     gc.disable()
     try:
+        warm_up(fn, warmup)
         t0 = time.perf_counter()
         e0.record(stream)
         for _ in range(steps):
@@ -296,6 +316,8 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0, cold=T
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
+        "warmup_policy": "at least `warmup` launches and at least %d ms of them" % round(
+            WARMUP_MIN_S * 1e3),
         "ms_per_step": round(wall_ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
