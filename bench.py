@@ -121,7 +121,11 @@ def warm_up(fn, warmup):
         if n % 8 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    _WARMED[0] = n
     return n
+
+
+_WARMED = [0]  # warm-up launches of the last timed region
 
 
 def time_kernel(fn, steps, warmup):
@@ -286,6 +290,7 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0, cold=T
             raise SystemExit("parity gate failed on %s: rel_l2=%.3e max_abs=%.3e"
                              % (name, rel, mab))
     wall_ms, kern_ms = time_kernel(fn, steps, warmup)
+    warmed = _WARMED[0]
     graph_ms = time_graph(fn, steps)
     single = {"warm": per_launch_us(fn, steps)}
     if cold:
@@ -318,6 +323,7 @@ def bench_workload(name, steps, warmup, check=True, cpu=True, cpu_s=10.0, cold=T
         "warmup": warmup,
         "warmup_policy": "at least `warmup` launches and at least %d ms of them" % round(
             WARMUP_MIN_S * 1e3),
+        "warmup_launches": warmed,
         "ms_per_step": round(wall_ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -367,7 +373,7 @@ def companion(name, steps, warmup, cold=False):
     rec = bench_workload(name, steps, warmup, check=True, cpu=False, cold=cold)
     return {k: rec[k] for k in ("value", "unit", "mfma_peak_frac", "ms_per_step", "kernel_us",
                                 "kernel_us_graph", "per_launch_us", "roofline", "parity_sampled",
-                                "inputs_sha256")} | {
+                                "inputs_sha256", "warmup_launches")} | {
         "shape_BTHWNH_HD": rec["config"]["shape_BTHWNH_HD"], "window": rec["config"]["window"],
         "family": rec["config"]["family"], "variant": rec["config"]["variant"],
         "workgroups": rec["config"]["workgroups"]}
@@ -485,6 +491,7 @@ def bench_rms_norm(launches=400, warmup=20, check=True, cpu_s=3.0):
             raise SystemExit("parity gate failed on the RMSNorm workload: worst relative "
                              "error %.3e" % worst)
     _, kern_ms = time_kernel(fn, launches, warmup)
+    warmed = _WARMED[0]
     kern_s = kern_ms * 1e-3
     tbytes = measured_traffic(wl.name, "rms_norm_%s_traffic.md", NORM_SOURCES)
     gbs = wl.bytes / kern_s / 1e9
@@ -502,7 +509,7 @@ def bench_rms_norm(launches=400, warmup=20, check=True, cpu_s=3.0):
     per_row = wl.bytes / wl.rows
     return {
         "workload": wl.name, "rows": wl.rows, "dim": wl.dim, "weight": True, "eps": NORM_EPS,
-        "launches": launches, "kernel_us": round(kern_ms * 1e3, 2),
+        "launches": launches, "warmup_launches": warmed, "kernel_us": round(kern_ms * 1e3, 2),
         "value": round(gbs, 1), "unit": "GB/s",
         "roofline": {
             "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -739,7 +746,7 @@ def main():
             "per_launch_us": lw["per_launch_us"],
             "roofline": lw["roofline"], "parity_sampled": lw["parity_sampled"],
             "inputs_sha256": lw["inputs_sha256"], "variant": lw["config"]["variant"],
-            "workgroups": lw["config"]["workgroups"]}
+            "workgroups": lw["config"]["workgroups"], "warmup_launches": lw["warmup_launches"]}
         # the pages' anisotropic wide-window benchmark grid, (3,5,27)
         ww = bench_workload("wide_w27", args.steps, args.warmup, check=not args.no_check,
                             cpu=False, cold=not args.no_cold)
@@ -747,7 +754,8 @@ def main():
             "shape_BTHWNH_HD": ww["config"]["shape_BTHWNH_HD"], "value": ww["value"],
             "unit": "TFLOP/s", "kernel_us": ww["kernel_us"],
             "kernel_us_graph": ww["kernel_us_graph"], "roofline": ww["roofline"],
-            "parity_sampled": ww["parity_sampled"], "variant": ww["config"]["variant"]}
+            "parity_sampled": ww["parity_sampled"], "variant": ww["config"]["variant"],
+            "warmup_launches": ww["warmup_launches"]}
         # a window wider than 33 along W (the shapes the pages' kernel refused)
         rec["wide_window_3x5x41"] = companion("wide_w41", args.steps, args.warmup)
         # a 19x19x19 window: the four-group rolling instantiation at head dim
