@@ -334,11 +334,18 @@ int pick_roll(const Geom& g, Launch* l) {
   // 24x32x32, 4 heads: 384 us against 1687 us for the general family;
   // (5,19,19) on 8x32x64: 88 against 317 us)
   static const int p64_large[] = {5, 46, 51, 50, 49, 58, 55, 56, 10, 22, 6, 7, 9, 62};
-  // head dim 128: 4x4 blocks (one 13-tile group) before the 2x8 two-group
-  // variants for near-cubic windows (11x11x11 on 16x48x64, 8 heads: 1018 us
-  // against 1299 us for variant 57 and 1632 us for variant 15); the 9-tile
-  // two-group 2x8 variant for wide windows (3x7x19: 1004 us against 1080 us)
-  static const int p128[] = {47, 25, 16, 57, 15, 14, 13, 29};
+  // head dim 128: past the 2x8 7-tile variants, two-plane blocks of 2x4
+  // queries in 8-wave workgroups of 8x4-query tiles (77: one 126 KB
+  // workgroup per CU, two waves per SIMD, where the 4-wave variants of
+  // 100-104 KB leave one): 16x64x96, 8 heads, (3,11,11) 501 against 830 us
+  // for 4x4 blocks (16), (5,9,9) 690 against 1120, (7,9,9) 842 against 1330;
+  // 11x11x11 on 16x48x64 636 against 912 us for the 4-wave two-plane
+  // variant (60) and 982 for 16, on 16x80x32 at 32 heads 2043 against 2984;
+  // then 4x4 blocks (one 13-tile group) before the 2x8 two-group variants
+  // for near-cubic windows (11x11x11 on 16x48x64, 8 heads: 1018 us against
+  // 1299 us for variant 57 and 1632 us for variant 15); the 9-tile two-group
+  // 2x8 variant for wide windows (3x7x19: 1004 us against 1080 us)
+  static const int p128[] = {47, 25, 77, 16, 57, 15, 14, 13, 29};
   // head dim 256: one-buffer variants (a two-buffer plane of 512-byte rows
   // does not fit LDS; measured 548 us against 862 us for the general family
   // on 16x64x96, 4 heads, (3,7,7))

@@ -161,3 +161,16 @@ def test_two_plane_tile_by_grid_length():
     for T, wh in [(16, 2), (24, 2), (32, 6), (79, 6)]:
         info = na.variant_info(na.plan((1, T, 96, 96, 8, 64), (11, 11, 11))["variant"])
         assert info["qh"] * info["qw"] == 8 and info["wh"] == wh, (T, info)
+
+
+def test_head_dim_128_two_plane_workgroups():
+    """Head dim 128, windows past the 2x8 7-tile variants: two-plane blocks in
+    8-wave workgroups of 8x4-query tiles (two waves per SIMD); (5,7,7) stays
+    on 2x8 blocks and the three-plane (3,7,7) on its staging-wave variant."""
+    shape = (1, 16, 64, 96, 8, 128)
+    for ks in [(11, 11, 11), (3, 11, 11), (7, 9, 9), (3, 7, 19)]:
+        info = na.variant_info(na.plan(shape, ks)["variant"])
+        assert (info["hd"], info["qh"] * info["qw"], info["wh"], info["wt"]) == (128, 8, 4, 2), ks
+        assert na.plan(shape, ks)["threads"] == 512
+    assert na.variant_info(na.plan(shape, (5, 7, 7))["variant"])["qw"] == 8
+    assert na.plan(shape, (3, 7, 7))["threads"] == 768
