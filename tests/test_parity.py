@@ -110,6 +110,28 @@ def test_workload_sampled_full_size(name):
         "output leaves the convex hull of the value rows"
 
 
+@pytest.mark.parametrize("shape,ks,wh", [
+    ((1, 48, 72, 80, 4, 64), (11, 11, 11), 6),   # 12x4-query tiles of two-plane blocks
+    ((1, 20, 56, 72, 4, 128), (11, 11, 11), 4),  # head dim 128, 8x4-query tiles
+    ((1, 16, 40, 72, 2, 128), (3, 7, 19), 4),
+])
+def test_two_plane_tiles_sampled(shape, ks, wh):
+    """The multi-row two-plane-block workgroups the planner takes on long
+    grids (head dim 64) and at head dim 128, on grids of hundreds of
+    workgroups in their default plans, checked on sampled outputs the oracle
+    computes one by one (borders included)."""
+    info = na.variant_info(na.plan(shape, ks)["variant"])
+    assert info["qh"] * info["qw"] == 8 and info["wh"] == wh
+    print("case two-plane tiles shape=%s window=%s" % (shape, ks), flush=True)
+    q, k, v = inputs_on_gpu(shape, 61)
+    out = run(q, k, v, ks)
+    pts = sample_points(shape, ks, 2000, 61)
+    ref = oracle.fwd_points(q.cpu(), k.cpu(), v.cpu(), ks, pts)
+    idx = tuple(torch.as_tensor(pts[:, i]) for i in range(5))
+    compare(out.cpu()[idx].to(torch.float64).numpy(), ref, "two-plane tiles %s" % (ks,))
+    assert torch.isfinite(out.float()).all()
+
+
 def test_large_window_full_grid():
     """The 11x11x11 workload at its full size, every output against the
     oracle, in the launch configuration the benchmark times."""
