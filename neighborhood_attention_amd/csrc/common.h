@@ -194,7 +194,8 @@ struct Launch {
   X(74, 16, 2, 4, 2, 2, 1, 11, 1, 1, 0, 0) \
   X(75, 128, 2, 4, 4, 2, 1, 5, 1, 2, 3, 4) \
   X(76, 64, 2, 4, 6, 2, 1, 11, 1, 2, 3, 0) \
-  X(77, 128, 2, 4, 4, 2, 1, 11, 1, 1, 0, 0)
+  X(77, 128, 2, 4, 4, 2, 1, 11, 1, 1, 0, 0) \
+  X(78, 128, 2, 8, 1, 8, 1, 9, 2, 1, 0, 0)
 
 struct RollVariant {
   int hd, qh, qw, wh, wt, ns, nk, ng, nbuf, occ, pw;

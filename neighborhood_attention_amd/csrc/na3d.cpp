@@ -344,8 +344,13 @@ int pick_roll(const Geom& g, Launch* l) {
   // then 4x4 blocks (one 13-tile group) before the 2x8 two-group variants
   // for near-cubic windows (11x11x11 on 16x48x64, 8 heads: 1018 us against
   // 1299 us for variant 57 and 1632 us for variant 15); the 9-tile two-group
-  // 2x8 variant for wide windows (3x7x19: 1004 us against 1080 us)
-  static const int p128[] = {47, 25, 77, 16, 57, 15, 14, 13, 29};
+  // 2x8 variant for wide windows (3x7x19: 1004 us against 1080 us), with 8
+  // phases along T in 8 waves (78: the same 147 KB of LDS, two waves per
+  // SIMD instead of one, bitwise the same outputs) before its 4-wave form
+  // (57): (13,13,13) on 16x32x32 at 8 heads 342 against 485 us, (3,5,27)
+  // and (3,5,35) on 16x64x128 1283 and 1335 against 1327 and 1393 us,
+  // (3,5,27) on 4x8x128 at 32 heads 168 against 174 us
+  static const int p128[] = {47, 25, 77, 16, 78, 57, 15, 14, 13, 29};
   // head dim 256: one-buffer variants (a two-buffer plane of 512-byte rows
   // does not fit LDS; measured 548 us against 862 us for the general family
   // on 16x64x96, 4 heads, (3,7,7))

@@ -174,3 +174,13 @@ def test_head_dim_128_two_plane_workgroups():
         assert na.plan(shape, ks)["threads"] == 512
     assert na.variant_info(na.plan(shape, (5, 7, 7))["variant"])["qw"] == 8
     assert na.plan(shape, (3, 7, 7))["threads"] == 768
+
+
+def test_head_dim_128_wide_windows_eight_phases():
+    """Head dim 128, windows whose 2x4-block union passes 11 tiles: 2x8
+    blocks in two 9-tile groups, 8 waves along T (two waves per SIMD at the
+    same 147 KB of LDS as the 4-wave form)."""
+    for shape, ks in [((1, 16, 32, 32, 8, 128), (13, 13, 13)), ((1, 16, 64, 128, 8, 128), (3, 5, 27)),
+                      ((1, 4, 8, 128, 32, 128), (3, 5, 35))]:
+        info = na.variant_info(na.plan(shape, ks)["variant"])
+        assert (info["hd"], info["qw"], info["wh"], info["wt"], info["ng"]) == (128, 8, 1, 8, 2), ks
