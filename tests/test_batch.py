@@ -65,6 +65,21 @@ def test_large_window_batch():
     check_batch(dims, 1, 64, (11, 11, 11), 320)
 
 
+@pytest.mark.parametrize("dims,HD,ks,shape_id", [
+    # 12x4-query tiles of two-plane blocks (head dim 64, grids of 32+ planes)
+    ([(1, 34, 20, 26), (1, 12, 13, 24), (1, 11, 11, 11)], 64, (11, 11, 11), (64, 8, 6, 2)),
+    # 8x4-query tiles of two-plane blocks at head dim 128
+    ([(1, 12, 16, 20), (1, 11, 11, 11)], 128, (11, 11, 11), (128, 8, 4, 2)),
+    # 2x8 blocks in two 9-tile groups, eight phases along T, head dim 128
+    ([(1, 14, 16, 24), (1, 13, 13, 13)], 128, (13, 13, 13), (128, 16, 1, 8)),
+])
+def test_multi_row_and_eight_phase_batches(dims, HD, ks, shape_id):
+    plan = na.plan_batch(dims, 1, HD, ks)
+    info = na.variant_info(plan["variant"])
+    assert (info["hd"], info["qh"] * info["qw"], info["wh"], info["wt"]) == shape_id
+    check_batch(dims, 1, HD, ks, 335)
+
+
 def test_wide_window_batch():
     dims = [(1, 4, 8, 64), (1, 3, 5, 27)]
     check_batch(dims, 2, 64, (3, 5, 27), 330)
