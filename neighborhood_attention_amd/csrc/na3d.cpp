@@ -425,6 +425,21 @@ int pick_roll(const Geom& g, Launch* l) {
       Launch alt;
       if (plan_roll(34, g, 0, &alt)) *l = alt;
     }
+    // three-plane windows on grids of 32 or more query planes with enough
+    // 8x8-query tiles to fill the chip without cutting the runs along T:
+    // 12-wave workgroups of those tiles (18: 4 block rows by 3 phases, one
+    // workgroup per CU), whose halo is re-read by fewer workgroups.  On
+    // 96x128 at 8 heads (3,7,7) 552 against 568 us at T = 32, 805 against
+    // 851 at 48, 1055 against 1138 at 64; 79x192x192 4205 against 4392 us;
+    // 64x96 at 32 heads equal.  Where the runs would be cut (64x96 at 8
+    // heads: 768 tiles) it is far slower (T = 64: 945 against 578 us), as
+    // on 16-plane grids
+    if (l->variant == 42 && g.KT == 3 && g.box.Tq >= 32) {
+      Launch alt;
+      if (plan_roll(18, g, 0, &alt) && alt.tiles_t == 1 &&
+          alt.wgs >= kTargetWorkgroups)
+        *l = alt;
+    }
     // query blocks over two planes (2x4 queries on each), for windows long
     // along T: where their smaller window union saves more tiles than the
     // extra key plane per block costs, i.e. (KT + 1) x 11 tiles per 16

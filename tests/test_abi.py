@@ -184,3 +184,14 @@ def test_head_dim_128_wide_windows_eight_phases():
                       ((1, 4, 8, 128, 32, 128), (3, 5, 35))]:
         info = na.variant_info(na.plan(shape, ks)["variant"])
         assert (info["hd"], info["qw"], info["wh"], info["wt"], info["ng"]) == (128, 8, 1, 8, 2), ks
+
+
+def test_three_plane_tile_by_grid_size():
+    """(3,7,7) at head dim 64: 12-wave 8x8-query tiles only on grids of 32 or
+    more planes whose 8x8 tiles fill the chip without cutting the runs
+    along T; 8-wave 4x8-query tiles otherwise."""
+    for shape, rows in [((1, 16, 96, 128, 8, 64), 4), ((1, 31, 96, 128, 8, 64), 4),
+                        ((1, 32, 96, 128, 8, 64), 8), ((1, 79, 192, 192, 8, 64), 8),
+                        ((1, 64, 64, 96, 8, 64), 4), ((1, 33, 64, 96, 8, 64), 4)]:
+        p = na.plan(shape, (3, 7, 7))
+        assert (p["tile_h"], p["tile_w"]) == (rows, 8), (shape, p)

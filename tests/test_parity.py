@@ -132,6 +132,23 @@ def test_two_plane_tiles_sampled(shape, ks, wh):
     assert torch.isfinite(out.float()).all()
 
 
+def test_three_plane_long_grid_sampled():
+    """(3,7,7) at head dim 64 on a 33-plane 96x128 grid in its default plan
+    (12-wave 8x8-query tiles), sampled outputs and borders against the
+    oracle."""
+    shape, ks = (1, 33, 96, 128, 8, 64), (3, 7, 7)
+    p = na.plan(shape, ks)
+    assert (p["tile_h"], p["tile_w"], p["threads"]) == (8, 8, 768)
+    print("case three-plane long grid shape=%s window=%s" % (shape, ks), flush=True)
+    q, k, v = inputs_on_gpu(shape, 63)
+    out = run(q, k, v, ks)
+    pts = sample_points(shape, ks, 3000, 63)
+    ref = oracle.fwd_points(q.cpu(), k.cpu(), v.cpu(), ks, pts)
+    idx = tuple(torch.as_tensor(pts[:, i]) for i in range(5))
+    compare(out.cpu()[idx].to(torch.float64).numpy(), ref, "three-plane long grid")
+    assert torch.isfinite(out.float()).all()
+
+
 def test_large_window_full_grid():
     """The 11x11x11 workload at its full size, every output against the
     oracle, in the launch configuration the benchmark times."""
